@@ -1,0 +1,222 @@
+"""Python binding of libbastion.so: argument marshalling only.
+
+Every function takes torch tensors that live on the GPU, allocates the output
+tensors with torch (device memory is PyTorch's job here), passes raw device
+pointers and the current HIP stream to the C ABI, and returns the outputs.
+No step of the computation happens in Python.  If the shared library is
+missing or fails to load, every entry raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbastion.so")
+
+OK, EINVAL, EUNSUPPORTED, EHIP, EWORKSPACE = 0, 1, 2, 3, 4
+Q_OK, Q_BAD_LOGITS, Q_EXHAUSTED = 0, 1, 2
+F32, BF16 = 0, 1
+
+_lib = None
+
+
+class BastionError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_status_string(status)} (status {status})")
+
+
+P = C.c_void_p
+I32, I64, F64, SZ = C.c_int32, C.c_int64, C.c_double, C.c_size_t
+
+
+class TreeOut(C.Structure):
+    _fields_ = [(n, P) for n in ("topk_ids", "topk_q", "row_max", "row_sum", "parent", "depth",
+                                 "token", "rho", "ahat", "n_nodes", "qstatus", "mask",
+                                 "position_ids")]
+
+
+class MixOut(C.Structure):
+    _fields_ = [(n, P) for n in ("prior_q", "chain_tokens", "qdep_chain", "cand_count",
+                                 "cand_tokens", "cand_q", "row_max", "row_sum")]
+
+
+def lib():
+    """The loaded library (torch's HIP runtime is loaded first, so both share it)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_diffusion_tree_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        L.bastion_abi_version.restype = I32
+        L.bastion_status_string.restype = C.c_char_p
+        L.bastion_status_string.argtypes = [I32]
+        L.bastion_workspace_bytes.restype = SZ
+        L.bastion_workspace_bytes.argtypes = [I32] * 7
+        L.bastion_workspace_init.restype = I32
+        L.bastion_workspace_init.argtypes = [P, SZ, P]
+        L.bastion_build_trees.restype = I32
+        L.bastion_build_trees.argtypes = [P, I32, I32, I32, I32, I64, I32, I32, I32, P, I64, F64,
+                                          P, C.POINTER(TreeOut), P, SZ, P]
+        L.bastion_budget_select.restype = I32
+        L.bastion_budget_select.argtypes = [P, P, I32, I32, I32, P, I64, F64, P, P, P]
+        L.bastion_tree_mask.restype = I32
+        L.bastion_tree_mask.argtypes = [P, P, I32, I32, P, P, P, P]
+        L.bastion_accept.restype = I32
+        L.bastion_accept.argtypes = [P, P, P, I32, I32, I32, P, P, P, P, P]
+        L.bastion_mixture_score.restype = I32
+        L.bastion_mixture_score.argtypes = [P, I32, P, I32, I32, I32, I32, I64, I32, I32,
+                                            C.POINTER(MixOut), C.POINTER(TreeOut), P, SZ, P]
+        _lib = L
+    return _lib
+
+
+def _status_string(s: int) -> str:
+    try:
+        return lib().bastion_status_string(s).decode()
+    except Exception:  # pragma: no cover - only when the library is absent
+        return "?"
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise BastionError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("logits must be float32 or bfloat16")
+
+
+class Workspace:
+    """Device scratch for the fused calls (grows on demand, zeroed once)."""
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(max(nbytes, 1 << 18), dtype=torch.uint8,
+                                   device=self.device or "cuda")
+            _check(lib().bastion_workspace_init(_ptr(self.buf), self.buf.numel(), _stream()),
+                   "bastion_workspace_init")
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _workspace(ws, device):
+    if ws is not None:
+        return ws
+    key = str(device)
+    if key not in _default_ws:
+        _default_ws[key] = Workspace(device)
+    return _default_ws[key]
+
+
+def alloc_tree_out(B, b, k, nmax, device, with_rows=True, with_mask=True):
+    W1 = nmax + 1
+    W = (W1 + 31) // 32
+    i32 = dict(dtype=torch.int32, device=device)
+    f32 = dict(dtype=torch.float32, device=device)
+    out = {}
+    if with_rows:
+        out.update(topk_ids=torch.empty((B, b, k), **i32), topk_q=torch.empty((B, b, k), **f32),
+                   row_max=torch.empty((B, b), **f32), row_sum=torch.empty((B, b), **f32))
+    out.update(parent=torch.empty((B, W1), **i32), depth=torch.empty((B, W1), **i32),
+               token=torch.empty((B, W1), **i32), rho=torch.empty((B, W1), **f32),
+               ahat=torch.empty((B, W1), dtype=torch.float64, device=device),
+               n_nodes=torch.empty((B,), **i32), qstatus=torch.empty((B,), **i32))
+    if with_mask:
+        out.update(mask=torch.empty((B, W1, W), **i32),   # uint32 bit rows, stored as int32
+                   position_ids=torch.empty((B, W1), **i32))
+    return out
+
+
+def _tree_struct(out):
+    return TreeOut(*[(_ptr(out[n]) if n in out else None) for n, _ in TreeOut._fields_])
+
+
+def build_trees(logits, k: int, nmax: int, nmin: int = 1, cost=None, l_ar: float = 1.0,
+                pos_base=None, with_mask: bool = True, out=None, ws=None):
+    """bastion_build_trees on logits [B, b, V] (float32 or bfloat16, on GPU)."""
+    _dev(logits, "logits")
+    if logits.dim() != 3 or logits.stride(2) != 1 or logits.stride(0) != logits.size(1) * logits.stride(1):
+        raise ValueError("logits must be [B, b, V] with unit stride over V and rows packed")
+    B, b, V = logits.shape
+    dt = _dtype_code(logits)
+    if out is None:
+        out = alloc_tree_out(B, b, k, nmax, logits.device, with_mask=with_mask)
+    cost_ptr, cstride = None, 0
+    if cost is not None:
+        _dev(cost, "cost")
+        if cost.dtype != torch.float64 or not cost.is_contiguous():
+            raise TypeError("cost must be a contiguous float64 GPU tensor")
+        cstride = 0 if cost.dim() == 1 or cost.size(0) == 1 else cost.size(1)
+        cost_ptr = _ptr(cost)
+    L = lib()
+    w = _workspace(ws, logits.device)
+    need = L.bastion_workspace_bytes(B, 1, b, V, k, nmax, dt)
+    buf = w.get(need)
+    st = _tree_struct(out)
+    _check(L.bastion_build_trees(_ptr(logits), dt, B, b, V, logits.stride(1), k, nmax, nmin,
+                                 cost_ptr, cstride, l_ar, _ptr(pos_base), C.byref(st),
+                                 _ptr(buf), buf.numel(), _stream()),
+           "bastion_build_trees")
+    return out
+
+
+def budget_select(ahat, n_avail, nmin: int, cost, l_ar: float = 1.0, with_curve: bool = True):
+    B, W1 = ahat.shape
+    nstar = torch.empty((B,), dtype=torch.int32, device=ahat.device)
+    s = torch.empty((B, W1), dtype=torch.float64, device=ahat.device) if with_curve else None
+    cstride = 0 if cost.dim() == 1 or cost.size(0) == 1 else cost.size(1)
+    _check(lib().bastion_budget_select(_ptr(ahat), _ptr(n_avail), B, W1 - 1, nmin, _ptr(cost),
+                                       cstride, l_ar, _ptr(nstar), _ptr(s), _stream()),
+           "bastion_budget_select")
+    return nstar, s
+
+
+def tree_mask(parent, n_nodes, pos_base=None):
+    B, W1 = parent.shape
+    W = (W1 + 31) // 32
+    mask = torch.empty((B, W1, W), dtype=torch.int32, device=parent.device)
+    pos = torch.empty((B, W1), dtype=torch.int32, device=parent.device)
+    _check(lib().bastion_tree_mask(_ptr(parent), _ptr(n_nodes), B, W1 - 1, _ptr(pos_base),
+                                   _ptr(mask), _ptr(pos), _stream()), "bastion_tree_mask")
+    return mask, pos
+
+
+def accept(parent, token, n_nodes, b: int, target):
+    B, W1 = parent.shape
+    dev = parent.device
+    alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    anodes = torch.empty((B, b + 1), dtype=torch.int32, device=dev)
+    bonus = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(lib().bastion_accept(_ptr(parent), _ptr(token), _ptr(n_nodes), B, b, W1 - 1,
+                                _ptr(target), _ptr(alen), _ptr(anodes), _ptr(bonus), _stream()),
+           "bastion_accept")
+    return alen, anodes, bonus

@@ -1,0 +1,203 @@
+// api.hip -- the extern "C" entry points of libbastion.so: argument
+// validation, workspace layout, launch planning and launches.  No call
+// allocates memory; every check happens before the first HIP call, so an
+// EINVAL / EUNSUPPORTED / EWORKSPACE return means nothing was enqueued.
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "device_common.hpp"
+
+#include "build_params.hpp"
+
+// launchers, defined next to their kernels
+
+hipError_t bastion_launch_build(const bastion::BuildParams &P, int dtype, hipStream_t s,
+                                int *smem_out);
+hipError_t bastion_launch_budget_select(const double *ahat, const int32_t *n_avail, int B, int nmax,
+                                        int nmin, const double *cost, int64_t cost_qstride,
+                                        double l_ar, int32_t *nstar, double *s_curve,
+                                        hipStream_t s);
+hipError_t bastion_launch_tree_mask(const int32_t *parent, const int32_t *n_nodes, int B,
+                                    int nmax, const int32_t *pos_base, uint32_t *mask,
+                                    int32_t *position_ids, hipStream_t s);
+hipError_t bastion_launch_accept(const int32_t *parent, const int32_t *token,
+                                 const int32_t *n_nodes, int B, int b, int nmax,
+                                 const int32_t *target, int32_t *accept_len,
+                                 int32_t *accept_nodes, int32_t *bonus, hipStream_t s);
+hipError_t bastion_launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t s);
+
+namespace {
+
+using namespace bastion;
+
+// Workspace layout.  The arrival counters sit at fixed offsets at the head
+// so that a workspace can be reused across shapes.
+constexpr size_t kTicketWords = 65536;
+constexpr size_t kRowTicketWords = 49152;            // per-row counters
+constexpr size_t kQueryTicketBase = kRowTicketWords;  // per-query counters
+constexpr size_t kTicketBytes = kTicketWords * 4;
+constexpr int kMaxSegments = 64;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int esize(int dtype) { return dtype == BASTION_BF16 ? 2 : 4; }
+
+struct Layout {
+    size_t row_status, partials, total;
+    int S;
+};
+
+// Segments per row: enough blocks to cover the machine (256 CUs, several
+// blocks each) without making a segment shorter than one 16-byte load per
+// thread.  BASTION_SEGMENTS overrides (tuning).
+int plan_segments(int64_t rows, int V, int dtype) {
+    int S = int((2048 + rows - 1) / rows);
+    const char *env = getenv("BASTION_SEGMENTS");
+    if (env && atoi(env) > 0) S = atoi(env);
+    const int64_t row_bytes = int64_t(V) * esize(dtype);
+    const int64_t by_size = row_bytes / 4096;
+    if (S > by_size) S = int(by_size);
+    if (S > kMaxSegments) S = kMaxSegments;
+    if (S < 1) S = 1;
+    if (S > 1 && rows > int64_t(kRowTicketWords)) S = 1;
+    return S;
+}
+
+Layout layout(int64_t rows, int k, int S) {
+    Layout L;
+    L.S = S;
+    L.row_status = kTicketBytes;
+    L.partials = align256(L.row_status + size_t(rows) * 4);
+    L.total = align256(L.partials + (S > 1 ? size_t(rows) * S * size_t(16 + 8 * k) : 0));
+    return L;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int32_t to_status(hipError_t e) { return e == hipSuccess ? BASTION_OK : BASTION_EHIP; }
+
+bool sizes_ok(int32_t B, int32_t b, int32_t V, int32_t k, int32_t nmax) {
+    return B >= 1 && B <= 16384 && b >= 1 && b <= kMaxB && k >= 1 && k <= kMaxK && V >= k &&
+           V <= kMaxV && nmax >= 1 && nmax <= kMaxNmax;
+}
+
+bool tree_out_ok(const bastion_tree_out *o, bool need_rows) {
+    if (!o) return false;
+    if (need_rows && (!o->topk_ids || !o->topk_q || !o->row_max || !o->row_sum)) return false;
+    if (!o->parent || !o->depth || !o->token || !o->rho || !o->ahat || !o->n_nodes || !o->qstatus)
+        return false;
+    if (o->mask && !o->position_ids) return false;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t bastion_abi_version(void) { return BASTION_ABI_VERSION; }
+
+const char *bastion_status_string(int32_t status) {
+    switch (status) {
+        case BASTION_OK: return "ok";
+        case BASTION_EINVAL: return "invalid argument";
+        case BASTION_EUNSUPPORTED: return "unsupported request";
+        case BASTION_EHIP: return "HIP runtime error";
+        case BASTION_EWORKSPACE: return "workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+size_t bastion_workspace_bytes(int32_t B, int32_t K, int32_t b, int32_t V, int32_t k,
+                               int32_t nmax, int32_t dtype) {
+    (void)nmax;
+    if (B < 1 || K < 1 || b < 1 || V < 1 || k < 1 || (dtype != BASTION_F32 && dtype != BASTION_BF16))
+        return 0;
+    const int64_t rows = int64_t(B) * K * b;
+    return layout(rows, k, plan_segments(rows, V, dtype)).total;
+}
+
+int32_t bastion_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+    if (!ws || !aligned16(ws)) return BASTION_EINVAL;
+    if (ws_bytes < kTicketBytes) return BASTION_EWORKSPACE;
+    return to_status(bastion_launch_fill_u32(static_cast<uint32_t *>(ws), kTicketWords, 0u,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int32_t bastion_build_trees(const void *logits, int32_t dtype, int32_t B, int32_t b, int32_t V,
+                            int64_t row_stride, int32_t k, int32_t nmax, int32_t nmin,
+                            const double *cost, int64_t cost_qstride, double l_ar,
+                            const int32_t *pos_base, const bastion_tree_out *out, void *ws,
+                            size_t ws_bytes, void *stream) {
+    if (!logits || (dtype != BASTION_F32 && dtype != BASTION_BF16)) return BASTION_EINVAL;
+    if (!sizes_ok(B, b, V, k, nmax) || nmin < 0 || nmin > nmax) return BASTION_EINVAL;
+    if (row_stride < V || (reinterpret_cast<uintptr_t>(logits) % esize(dtype)) != 0)
+        return BASTION_EINVAL;
+    if (!tree_out_ok(out, true)) return BASTION_EINVAL;
+    if (cost && (cost_qstride < 0 || !(l_ar > 0.0) || l_ar > 1e300)) return BASTION_EINVAL;
+    const int64_t rows = int64_t(B) * b;
+    const int S = plan_segments(rows, V, dtype);
+    const Layout L = layout(rows, k, S);
+    if (!ws || !aligned16(ws) || ws_bytes < L.total) return BASTION_EWORKSPACE;
+
+    BuildParams P;
+    memset(&P, 0, sizeof P);
+    char *w = static_cast<char *>(ws);
+    P.logits = static_cast<const char *>(logits);
+    P.row_stride_bytes = row_stride * esize(dtype);
+    P.B = B; P.b = b; P.V = V; P.k = k; P.nmax = nmax; P.nmin = nmin; P.S = S;
+    P.cost = cost; P.cost_qstride = cost_qstride; P.l_ar = l_ar; P.pos_base = pos_base;
+    P.topk_ids = out->topk_ids; P.topk_q = out->topk_q; P.row_max = out->row_max;
+    P.row_sum = out->row_sum; P.parent = out->parent; P.depth = out->depth;
+    P.token = out->token; P.rho = out->rho; P.ahat = out->ahat; P.n_nodes = out->n_nodes;
+    P.qstatus = out->qstatus; P.mask = out->mask; P.position_ids = out->position_ids;
+    P.row_ticket = reinterpret_cast<uint32_t *>(w);
+    P.query_ticket = reinterpret_cast<uint32_t *>(w) + kQueryTicketBase;
+    P.row_status = reinterpret_cast<int32_t *>(w + L.row_status);
+    P.partials = w + L.partials;
+    P.partial_bytes = 16 + 8 * k;
+    return to_status(bastion_launch_build(P, dtype, static_cast<hipStream_t>(stream), nullptr));
+}
+
+int32_t bastion_budget_select(const double *ahat, const int32_t *n_avail, int32_t B, int32_t nmax,
+                              int32_t nmin, const double *cost, int64_t cost_qstride, double l_ar,
+                              int32_t *nstar, double *s_curve, void *stream) {
+    if (!ahat || !n_avail || !cost || !nstar) return BASTION_EINVAL;
+    if (B < 1 || nmax < 1 || nmax > kMaxNmax || nmin < 0 || nmin > nmax) return BASTION_EINVAL;
+    if (cost_qstride < 0 || !(l_ar > 0.0) || l_ar > 1e300) return BASTION_EINVAL;
+    return to_status(bastion_launch_budget_select(ahat, n_avail, B, nmax, nmin, cost, cost_qstride,
+                                                  l_ar, nstar, s_curve,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int32_t bastion_tree_mask(const int32_t *parent, const int32_t *n_nodes, int32_t B, int32_t nmax,
+                          const int32_t *pos_base, uint32_t *mask, int32_t *position_ids,
+                          void *stream) {
+    if (!parent || !n_nodes || !mask || !position_ids) return BASTION_EINVAL;
+    if (B < 1 || nmax < 1 || nmax > kMaxNmax) return BASTION_EINVAL;
+    return to_status(bastion_launch_tree_mask(parent, n_nodes, B, nmax, pos_base, mask,
+                                              position_ids, static_cast<hipStream_t>(stream)));
+}
+
+int32_t bastion_accept(const int32_t *parent, const int32_t *token, const int32_t *n_nodes,
+                       int32_t B, int32_t b, int32_t nmax, const int32_t *target,
+                       int32_t *accept_len, int32_t *accept_nodes, int32_t *bonus, void *stream) {
+    if (!parent || !token || !n_nodes || !target || !accept_len || !accept_nodes || !bonus)
+        return BASTION_EINVAL;
+    if (B < 1 || b < 1 || b > kMaxB || nmax < 1 || nmax > kMaxNmax) return BASTION_EINVAL;
+    return to_status(bastion_launch_accept(parent, token, n_nodes, B, b, nmax, target, accept_len,
+                                           accept_nodes, bonus, static_cast<hipStream_t>(stream)));
+}
+
+int32_t bastion_mixture_score(const void *branch_logits, int32_t dtype, const float *prior_logits,
+                              int32_t B, int32_t K, int32_t b, int32_t V, int64_t row_stride,
+                              int32_t k, int32_t nmax, const bastion_mixture_out *mix,
+                              const bastion_tree_out *tree, void *ws, size_t ws_bytes,
+                              void *stream) {
+    (void)branch_logits; (void)dtype; (void)prior_logits; (void)B; (void)K; (void)b; (void)V;
+    (void)row_stride; (void)k; (void)nmax; (void)mix; (void)tree; (void)ws; (void)ws_bytes;
+    (void)stream;
+    return BASTION_EUNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,31 @@
+// build_params.hpp -- kernel arguments of the fused build kernel, shared by
+// the kernel (build_trees.hip) and the entry points (api.hip).
+#pragma once
+
+#include <stdint.h>
+
+namespace bastion {
+
+struct BuildParams {
+    const char *logits;
+    int64_t row_stride_bytes;
+    int B, b, V, k, nmax, nmin, S;
+    const double *cost;
+    int64_t cost_qstride;
+    double l_ar;
+    const int32_t *pos_base;
+    int32_t *topk_ids;
+    float *topk_q, *row_max, *row_sum;
+    int32_t *parent, *depth, *token;
+    float *rho;
+    double *ahat;
+    int32_t *n_nodes, *qstatus;
+    uint32_t *mask;
+    int32_t *position_ids;
+    uint32_t *row_ticket, *query_ticket;
+    int32_t *row_status;
+    char *partials;       // [rows, S] records of kPartialBytes(k)
+    int partial_bytes;
+};
+
+}  // namespace bastion

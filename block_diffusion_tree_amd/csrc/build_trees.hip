@@ -1,0 +1,755 @@
+// build_trees.hip -- the fused gfx950 kernel behind bastion_build_trees.
+//
+// One launch does, for logits [B, b, V]:
+//   1. stream every row once from HBM (16-byte loads, 4 waves per block,
+//      each row split into S segments), keeping an online softmax
+//      (max / rescaled sum, one exp per element) and a filtered top-k
+//      (per-wave threshold; the few elements that beat it go through LDS);
+//   2. merge the S segment results of a row in the block that finishes the
+//      row last (arrival ticket), writing q = exp(l - M) / S for its top-k;
+//   3. in the block that finishes a query's last row (second ticket), build
+//      the best-first tree (Bastion, Methodology 1-2: rho products, A_hat),
+//      apply the online stop of Methodology 3, and emit the pop-order tree,
+//      the ancestor mask and the position ids.
+// Nothing waits on another block, so the grid needs no co-residency.
+#include "device_common.hpp"
+#include "build_params.hpp"
+
+namespace bastion {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kThreads = 256;               // 4 waves
+constexpr int kWavesPerBlock = kThreads / kWave;
+constexpr int kCap = 256;                   // per-wave candidate buffer (keys)
+
+
+
+// storage-type traits ------------------------------------------------------
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static constexpr int kPerVec = 4;
+    static constexpr uint32_t kNegInfWord = 0xFF800000u;
+    __device__ static __forceinline__ void decode(u32x4 r, float *f) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[j] = __uint_as_float(r[j]);
+    }
+    __device__ static __forceinline__ float at(const char *p, int64_t elem) {
+        return reinterpret_cast<const float *>(p)[elem];
+    }
+};
+template <> struct Elem<__bf16> {
+    static constexpr int kPerVec = 8;
+    static constexpr uint32_t kNegInfWord = 0xFF80FF80u;
+    __device__ static __forceinline__ void decode(u32x4 r, float *f) {
+        bf16x8 h = __builtin_bit_cast(bf16x8, r);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = (float)h[j];
+    }
+    __device__ static __forceinline__ float at(const char *p, int64_t elem) {
+        return (float)reinterpret_cast<const __bf16 *>(p)[elem];
+    }
+};
+
+template <int U>
+struct WaveScratch {
+    u32x4 stage_raw[kWave * U];
+    int32_t stage_vec[kWave * U];
+    uint64_t cand[kCap];
+};
+
+// ---------------------------------------------------------------------------
+// Per-wave state of the streaming stage.
+// ---------------------------------------------------------------------------
+struct LaneSoftmax {
+    float m;   // running max of this lane's elements
+    float c;   // scale_ref(m)
+    float s;   // sum of 2^(l*log2e - c)
+};
+
+template <typename T, int U>
+struct Streamer {
+    WaveScratch<U> *ws;
+    int k;
+    float thv;     // float form of the wave threshold (-inf: none yet)
+    uint64_t thk;  // the wave's current k-th best key (0: fewer than k so far)
+    int cnt;       // keys in ws->cand
+    int nstage;
+    int head;      // elements of the row before its first 16-byte aligned vector
+
+    __device__ void compact() {
+        uint64_t kth;
+        cnt = wave_select_topk<kCap / kWave>(ws->cand, cnt, k, kth);
+        thk = kth;
+        thv = kth ? topk_key_value(kth) : -INFINITY;
+    }
+
+    // Append the keys of the staged vectors that beat the threshold.
+    __device__ void drain_stage() {
+        constexpr int E = Elem<T>::kPerVec;
+        const int lane = lane_id();
+        const int total = nstage * E;
+        for (int base = 0; base < total; base += kWave) {
+            if (cnt + kWave > kCap) compact();
+            const int e = base + lane;
+            const bool ok = e < total;
+            uint64_t key = 0;
+            if (ok) {
+                const int sv = e / E, sj = e - sv * E;
+                float f[E];
+                Elem<T>::decode(ws->stage_raw[sv], f);
+                float v = f[0];
+#pragma unroll
+                for (int j = 1; j < E; ++j) v = (sj == j) ? f[j] : v;
+                key = topk_key(v, uint32_t(head + ws->stage_vec[sv] * E + sj));
+            }
+            const bool p = ok && key > thk;
+            const uint64_t msk = __ballot(p);
+            if (p) ws->cand[cnt + popc64(msk & lanemask_lt())] = key;
+            cnt += popc64(msk);
+            wave_sync();
+        }
+        nstage = 0;
+    }
+
+    // Candidates that are single elements (the scalar tail of a row).
+    __device__ void offer_scalar(bool ok, float v, uint32_t token) {
+        if (cnt + kWave > kCap) compact();
+        uint64_t key = ok ? topk_key(v, token) : 0;
+        const bool p = ok && key > thk;
+        const uint64_t msk = __ballot(p);
+        if (p) ws->cand[cnt + popc64(msk & lanemask_lt())] = key;
+        cnt += popc64(msk);
+        wave_sync();
+    }
+
+    // One tile: U vectors per lane.  raw[u] is row vector vbase + u * 256 +
+    // threadIdx.x; valid[u] false marks padding (filled with -inf).
+    __device__ __forceinline__ void tile(const u32x4 *raw, int vbase, const bool *valid,
+                                         LaneSoftmax &sm) {
+        constexpr int E = Elem<T>::kPerVec;
+        float f[U][E];
+        float vmax[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            Elem<T>::decode(raw[u], f[u]);
+            float a = f[u][0];
+#pragma unroll
+            for (int j = 1; j < E; ++j) a = fmaxf(a, f[u][j]);
+            vmax[u] = a;
+        }
+        float tmax = vmax[0];
+#pragma unroll
+        for (int u = 1; u < U; ++u) tmax = fmaxf(tmax, vmax[u]);
+        const float m_new = fmaxf(sm.m, tmax);
+        const float c_new = scale_ref(m_new);
+        float acc = sm.s * __builtin_amdgcn_exp2f(sm.c - c_new);
+        float part[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float e[E];
+#pragma unroll
+            for (int j = 0; j < E; ++j)
+                e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[u][j], kLog2e, -c_new));
+            // pairwise sum of the vector
+#pragma unroll
+            for (int w = E / 2; w >= 1; w >>= 1)
+#pragma unroll
+                for (int j = 0; j < w; ++j) e[j] += e[j + w];
+            part[u] = e[0];
+        }
+#pragma unroll
+        for (int w = U / 2; w >= 1; w >>= 1)
+#pragma unroll
+            for (int u = 0; u < w; ++u) part[u] += part[u + w];
+        sm.s = acc + part[0];
+        sm.m = m_new;
+        sm.c = c_new;
+
+        bool pass[U];
+        bool any = false;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            pass[u] = valid[u] && vmax[u] >= thv;
+            any |= pass[u];
+        }
+        if (__ballot(any)) {
+            const uint64_t lt = lanemask_lt();
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint64_t msk = __ballot(pass[u]);
+                if (msk) {
+                    if (pass[u]) {
+                        const int slot = nstage + popc64(msk & lt);
+                        ws->stage_raw[slot] = raw[u];
+                        ws->stage_vec[slot] = vbase + u * kThreads + int(threadIdx.x);
+                    }
+                    nstage += popc64(msk);
+                }
+            }
+            wave_sync();
+            drain_stage();
+        }
+    }
+};
+
+template <typename T>
+__device__ __forceinline__ u32x4 load_vec(const char *row, int v) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row) + v);
+}
+
+// ---------------------------------------------------------------------------
+// Segment of a row -> (m, s relative to scale_ref(m)) and the top-k keys,
+// left in wave 0's candidate buffer (cand[0..nsel)) of the block.
+// ---------------------------------------------------------------------------
+struct SegmentResult {
+    float m, s;
+    int nsel;
+};
+
+template <typename T, int U>
+__device__ SegmentResult stream_segment(const BuildParams &P, const char *row, int seg, char *smem) {
+    constexpr int E = Elem<T>::kPerVec;
+    constexpr int ES = int(sizeof(T));
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    WaveScratch<U> *scr = reinterpret_cast<WaveScratch<U> *>(smem);
+
+    // The row is split into: `head` elements up to the first 16-byte
+    // boundary, `nvec` aligned vectors, and `tail` elements after them.
+    const int V = P.V;
+    int head = int(((16u - (uint32_t(reinterpret_cast<uintptr_t>(row)) & 15u)) & 15u) / ES);
+    head = head > V ? V : head;
+    const int nvec = (V - head) / E;
+    const int tail = V - head - nvec * E;
+    const char *rowv = row + head * ES;
+
+    // vectors [v_lo, v_hi) of this segment
+    const int per = nvec / P.S, rem = nvec % P.S;
+    const int v_lo = seg * per + (seg < rem ? seg : rem);
+    const int v_hi = v_lo + per + (seg < rem ? 1 : 0);
+
+    Streamer<T, U> st;
+    st.ws = &scr[wv];
+    st.k = P.k;
+    st.thv = -INFINITY;
+    st.thk = 0;
+    st.cnt = 0;
+    st.nstage = 0;
+    st.head = head;
+    LaneSoftmax sm{-INFINITY, scale_ref(-INFINITY), 0.0f};
+
+    const int span = kThreads * U;
+    const int n = v_hi - v_lo;
+    const int ntiles = n / span;
+    bool all[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) all[u] = true;
+    const int vlo = v_lo;
+    u32x4 A[U], Bv[U];
+    auto fill = [&](u32x4 *dst, int t) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) dst[u] = load_vec<T>(rowv, vlo + t * span + u * kThreads + tid);
+    };
+    if (ntiles > 0) fill(A, 0);
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+        fill(Bv, t + 1);
+        st.tile(A, vlo + t * span, all, sm);
+        if (t + 2 < ntiles) fill(A, t + 2);
+        st.tile(Bv, vlo + (t + 1) * span, all, sm);
+    }
+    if (t < ntiles) st.tile(A, vlo + t * span, all, sm);
+    // ragged tile
+    {
+        bool ok[U];
+        bool anyv = false;
+        const int vb = vlo + ntiles * span;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int vi = vb + u * kThreads + tid;
+            ok[u] = vi < v_hi;
+            anyv |= ok[u];
+            const u32x4 ninf = {Elem<T>::kNegInfWord, Elem<T>::kNegInfWord,
+                                Elem<T>::kNegInfWord, Elem<T>::kNegInfWord};
+            A[u] = ok[u] ? load_vec<T>(rowv, vi) : ninf;
+        }
+        if (__ballot(anyv)) st.tile(A, vb, ok, sm);
+    }
+    // unaligned head and tail of the row (fewer than 2E elements), handled
+    // by wave 0 of the last segment
+    if (seg == P.S - 1 && (head + tail) > 0 && wv == 0) {
+        const bool ok = lane < head + tail;
+        const int elem = lane < head ? lane : head + nvec * E + (lane - head);
+        const float v = ok ? Elem<T>::at(row, elem) : -INFINITY;
+        const float m_new = fmaxf(sm.m, v);
+        const float c_new = scale_ref(m_new);
+        sm.s = sm.s * __builtin_amdgcn_exp2f(sm.c - c_new) +
+               (ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(v, kLog2e, -c_new)) : 0.0f);
+        sm.m = m_new;
+        sm.c = c_new;
+        st.offer_scalar(ok, v, uint32_t(elem));
+    }
+    // per-wave final selection
+    if (st.cnt > P.k || st.thk == 0) st.compact();
+
+    // ---- block merge: softmax state ----
+    __shared__ float red_m[kWavesPerBlock], red_s[kWavesPerBlock];
+    __shared__ int red_n[kWavesPerBlock];
+    const float wm = wave_max_f32(sm.m);
+    const float wc = scale_ref(wm);
+    const float ws_ = wave_sum_f32(sm.s * __builtin_amdgcn_exp2f(sm.c - wc));
+    if (lane == 0) {
+        red_m[wv] = wm;
+        red_s[wv] = ws_;
+        red_n[wv] = st.cnt;
+    }
+    __syncthreads();
+    SegmentResult res;
+    float M = red_m[0];
+#pragma unroll
+    for (int i = 1; i < kWavesPerBlock; ++i) M = fmaxf(M, red_m[i]);
+    const float C = scale_ref(M);
+    float Ssum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kWavesPerBlock; ++i)
+        Ssum += red_s[i] * __builtin_amdgcn_exp2f(scale_ref(red_m[i]) - C);
+    res.m = M;
+    res.s = Ssum;
+    // ---- block merge: top-k (wave 0 gathers the other waves' keys) ----
+    if (wv == 0) {
+        int total = red_n[0];
+        for (int w = 1; w < kWavesPerBlock; ++w) {
+            const int nw = red_n[w];
+            if (lane < nw) scr[0].cand[total + lane] = scr[w].cand[lane];
+            total += nw;
+        }
+        wave_sync();
+        uint64_t kth;
+        res.nsel = wave_select_topk<kCap / kWave>(scr[0].cand, total, P.k, kth);
+    }
+    return res;  // res.nsel valid in wave 0 only
+}
+
+// ---------------------------------------------------------------------------
+// Arrival ticket: the last of `total` blocks to arrive gets true.  Every
+// thread fences its own stores before the count; the winner fences again
+// before reading what the others wrote.  The counter is reset to 0 for the
+// next call.
+// ---------------------------------------------------------------------------
+__device__ bool arrive_last(uint32_t *ticket, uint32_t total) {
+    __shared__ int flag;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old = atomicAdd(ticket, 1u);
+        const bool last = (old == total - 1);
+        if (last) atomicExch(ticket, 0u);
+        flag = last;
+    }
+    __syncthreads();
+    const bool last = flag != 0;
+    if (last) __threadfence();
+    return last;
+}
+
+// ---------------------------------------------------------------------------
+// Tree stage.  LDS layout (byte offsets computed by tree_layout()).
+// ---------------------------------------------------------------------------
+struct TreeLayout {
+    int qtab, ttab, par, dep, tok, rho, nxt, popm, slow, ahat, cost, total;
+};
+
+__host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
+
+__host__ __device__ inline TreeLayout tree_layout(int b, int k, int nmax) {
+    TreeLayout L;
+    const int nn = nmax + 2;
+    int o = 0;
+    L.qtab = o; o = align16(o + 4 * b * k);
+    L.ttab = o; o = align16(o + 4 * b * k);
+    L.par = o;  o = align16(o + 4 * nn);
+    L.dep = o;  o = align16(o + 4 * nn);
+    L.tok = o;  o = align16(o + 4 * nn);
+    L.rho = o;  o = align16(o + 4 * nn);
+    L.nxt = o;  o = align16(o + 4 * nn);
+    L.popm = o; o = align16(o + 4 * nn);
+    L.slow = o; o = align16(o + 4 * nn);
+    L.ahat = o; o = align16(o + 8 * nn);
+    L.cost = o; o = align16(o + 8 * nn);
+    L.total = o;
+    return L;
+}
+
+// The frontier holds one key per popped node p (slot p): p's best child
+// that has not been popped yet.  Slot p lives in lane p % 64 of register
+// p / 64.
+template <int R>
+struct Frontier {
+    uint64_t key[R];
+    __device__ __forceinline__ void clear() {
+#pragma unroll
+        for (int r = 0; r < R; ++r) key[r] = 0;
+    }
+    __device__ __forceinline__ void set(int slot, uint64_t v) {
+        const int lane = lane_id();
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (slot == r * kWave + lane) key[r] = v;
+    }
+    __device__ __forceinline__ uint64_t best() const {
+        uint64_t m = key[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r) m = key[r] > m ? key[r] : m;
+        return wave_max_u64(m);
+    }
+};
+
+struct TreeCtx {
+    float *qtab;
+    int32_t *ttab, *par, *dep, *tok, *nxt, *slow;
+    uint32_t *popm;
+    float *rho;
+    double *ahat, *cost;
+    int b, k;
+};
+
+// Offer node n's first child (in pop order among its siblings); node n has
+// rho rn and depth dn < b.  Siblings are normally already in pop order by
+// rank j (q non-increasing); if rounding ties put a larger token first, the
+// node is marked slow and its children are served by argmax over ranks.
+__device__ __forceinline__ uint64_t first_child(const TreeCtx &T, int n, float rn, int dn) {
+    const int lane = lane_id();
+    const bool in = lane < T.k;
+    uint64_t key = 0;
+    if (in) {
+        const float pr = __fmul_rn(rn, T.qtab[dn * T.k + lane]);
+        key = tree_key(pr, dn + 1, T.ttab[dn * T.k + lane], n);
+    }
+    const uint64_t nextk = __shfl_down(key, 1, kWave);
+    const bool bad = (lane + 1 < T.k) && !(key > nextk);
+    const bool slow = __ballot(bad) != 0;
+    uint64_t first;
+    int rank;
+    if (!slow) {
+        first = __shfl(key, 0, kWave);
+        rank = 0;
+    } else {
+        first = wave_max_u64(key);
+        rank = __ffsll((unsigned long long)__ballot(in && key == first)) - 1;
+    }
+    if (lane == 0) {
+        T.nxt[n] = rank;
+        T.slow[n] = slow ? 1 : 0;
+        T.popm[n] = 0u;
+    }
+    return first;
+}
+
+// Node p's offered child was just popped; return p's next offer (0: none).
+__device__ __forceinline__ uint64_t next_child(const TreeCtx &T, int p, int dchild) {
+    const int lane = lane_id();
+    const float rp = T.rho[p];
+    const int pos = dchild - 1;
+    const int cur = T.nxt[p];
+    if (!T.slow[p]) {
+        const int c = cur + 1;
+        uint64_t key = 0;
+        if (c < T.k) key = tree_key(__fmul_rn(rp, T.qtab[pos * T.k + c]), dchild,
+                                    T.ttab[pos * T.k + c], p);
+        if (lane == 0) T.nxt[p] = c;
+        return key;
+    }
+    const uint32_t popped = T.popm[p] | (1u << cur);
+    const bool in = lane < T.k && !((popped >> lane) & 1u);
+    uint64_t key = 0;
+    if (in) key = tree_key(__fmul_rn(rp, T.qtab[pos * T.k + lane]), dchild,
+                           T.ttab[pos * T.k + lane], p);
+    const uint64_t best = wave_max_u64(key);
+    const int rank = best ? __ffsll((unsigned long long)__ballot(in && key == best)) - 1 : 0;
+    if (lane == 0) {
+        T.popm[p] = popped;
+        T.nxt[p] = rank;
+    }
+    return best;
+}
+
+template <int R>
+__device__ void tree_stage(const BuildParams &P, int q, char *smem) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const TreeLayout L = tree_layout(P.b, P.k, P.nmax);
+    TreeCtx T;
+    T.qtab = reinterpret_cast<float *>(smem + L.qtab);
+    T.ttab = reinterpret_cast<int32_t *>(smem + L.ttab);
+    T.par = reinterpret_cast<int32_t *>(smem + L.par);
+    T.dep = reinterpret_cast<int32_t *>(smem + L.dep);
+    T.tok = reinterpret_cast<int32_t *>(smem + L.tok);
+    T.rho = reinterpret_cast<float *>(smem + L.rho);
+    T.nxt = reinterpret_cast<int32_t *>(smem + L.nxt);
+    T.popm = reinterpret_cast<uint32_t *>(smem + L.popm);
+    T.slow = reinterpret_cast<int32_t *>(smem + L.slow);
+    T.ahat = reinterpret_cast<double *>(smem + L.ahat);
+    T.cost = reinterpret_cast<double *>(smem + L.cost);
+    T.b = P.b;
+    T.k = P.k;
+    __shared__ int s_bad, s_nstar, s_status;
+
+    const int bk = P.b * P.k;
+    const int64_t tk0 = int64_t(q) * bk;
+    for (int e = tid; e < bk; e += kThreads) {
+        T.qtab[e] = P.topk_q[tk0 + e];
+        T.ttab[e] = P.topk_ids[tk0 + e];
+    }
+    const bool online = P.cost != nullptr;
+    if (online)
+        for (int e = tid; e <= P.nmax; e += kThreads)
+            T.cost[e] = P.cost[int64_t(q) * P.cost_qstride + e];
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+    if (tid < P.b && P.row_status[int64_t(q) * P.b + tid] != BASTION_Q_OK) atomicOr(&s_bad, 1);
+    __syncthreads();
+    const bool bad = s_bad != 0;
+
+    if (!bad && wv == 0) {
+        Frontier<R> F;
+        F.clear();
+        // root
+        if (lane == 0) {
+            T.par[0] = -1;
+            T.dep[0] = 0;
+            T.tok[0] = -1;
+            T.rho[0] = 1.0f;
+            T.ahat[0] = 1.0;
+        }
+        wave_sync();
+        F.set(0, first_child(T, 0, 1.0f, 0));
+        wave_sync();
+        int count = 0, nstar = -1, status = BASTION_Q_OK;
+        double ah = 1.0;
+        double s_prev = online ? (1.0 * P.l_ar) / T.cost[0] : 0.0;
+        while (true) {
+            const uint64_t top = F.best();
+            if (top == 0) {
+                nstar = count;
+                status = count < P.nmax ? BASTION_Q_EXHAUSTED : BASTION_Q_OK;
+                break;
+            }
+            const int p = tree_key_parent(top);
+            const int d = tree_key_depth(top);
+            const int tkn = tree_key_token(top);
+            const float r = tree_key_rho(top);
+            const int n = count + 1;
+            const double ah_n = ah + double(r);
+            if (online) {
+                const double s_n = (ah_n * P.l_ar) / T.cost[n];
+                if (n - 1 >= P.nmin && s_n < s_prev) {
+                    nstar = n - 1;
+                    break;
+                }
+                s_prev = s_n;
+            }
+            count = n;
+            ah = ah_n;
+            if (lane == 0) {
+                T.par[n] = p;
+                T.dep[n] = d;
+                T.tok[n] = tkn;
+                T.rho[n] = r;
+                T.ahat[n] = ah_n;
+            }
+            wave_sync();
+            const uint64_t np = next_child(T, p, d);
+            wave_sync();
+            F.set(p, np);
+            if (count == P.nmax) {
+                nstar = count;
+                break;
+            }
+            if (d < P.b) {
+                F.set(n, first_child(T, n, r, d));
+                wave_sync();
+            }
+        }
+        if (lane == 0) {
+            s_nstar = nstar;
+            s_status = status;
+        }
+    }
+    __syncthreads();
+    const int nstar = bad ? 0 : s_nstar;
+    const int status = bad ? BASTION_Q_BAD_LOGITS : s_status;
+    const int W1 = P.nmax + 1;
+    const int64_t o = int64_t(q) * W1;
+    for (int i = tid; i < W1; i += kThreads) {
+        const bool v = i <= nstar && !bad;
+        P.parent[o + i] = v ? (i == 0 ? -1 : T.par[i]) : -1;
+        P.depth[o + i] = v ? (i == 0 ? 0 : T.dep[i]) : -1;
+        P.token[o + i] = v ? (i == 0 ? -1 : T.tok[i]) : -1;
+        P.rho[o + i] = v ? (i == 0 ? 1.0f : T.rho[i]) : 0.0f;
+        P.ahat[o + i] = v ? (i == 0 ? 1.0 : T.ahat[i]) : 0.0;
+    }
+    if (bad && tid == 0) {
+        P.parent[o] = -1;
+        P.depth[o] = 0;
+        P.token[o] = -1;
+        P.rho[o] = 1.0f;
+        P.ahat[o] = 1.0;
+    }
+    if (tid == 0) {
+        P.n_nodes[q] = nstar;
+        P.qstatus[q] = status;
+    }
+    if (P.mask) {
+        const int W = (W1 + 31) / 32;
+        const int32_t pb = P.pos_base ? P.pos_base[q] : 0;
+        for (int e = tid; e < W1 * W; e += kThreads) {
+            const int i = e / W, w = e - i * W;
+            uint32_t bits = 0;
+            int steps = 0;
+            if (i <= nstar) {
+                int j = i;
+                if (j / 32 == w) bits |= 1u << (j & 31);
+                while (j > 0 && steps < P.b) {
+                    j = T.par[j];
+                    ++steps;
+                    if (j / 32 == w) bits |= 1u << (j & 31);
+                }
+            }
+            P.mask[(o + i) * W + w] = bits;
+            if (w == 0) P.position_ids[o + i] = i <= nstar ? pb + steps : -1;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The kernel.  Block x handles segment x % S of row x / S.
+// ---------------------------------------------------------------------------
+constexpr int partial_bytes(int k) { return 16 + 8 * k; }
+
+template <typename T, int U, int R>
+__global__ __launch_bounds__(kThreads, 4) void build_trees_kernel(BuildParams P) {
+    extern __shared__ __align__(16) char smem[];
+    const int row = blockIdx.x / P.S;
+    const int seg = blockIdx.x - row * P.S;
+    const int q = row / P.b;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const char *rowp = P.logits + int64_t(row) * P.row_stride_bytes;
+
+    SegmentResult sr = stream_segment<T, U>(P, rowp, seg, smem);
+    WaveScratch<U> *scr = reinterpret_cast<WaveScratch<U> *>(smem);
+    uint64_t *cand = scr[0].cand;
+
+    float M = sr.m, Ssum = sr.s;
+    int nsel = sr.nsel;
+    if (P.S > 1) {
+        char *rec = P.partials + (int64_t(row) * P.S + seg) * P.partial_bytes;
+        if (wv == 0) {
+            if (lane == 0) {
+                reinterpret_cast<float *>(rec)[0] = M;
+                reinterpret_cast<float *>(rec)[1] = Ssum;
+                reinterpret_cast<int32_t *>(rec)[2] = nsel;
+            }
+            if (lane < P.k) reinterpret_cast<uint64_t *>(rec + 16)[lane] = lane < nsel ? cand[lane] : 0;
+        }
+        if (!arrive_last(P.row_ticket + row, uint32_t(P.S))) return;
+        // merge the S segment records of this row (wave 0)
+        if (wv == 0) {
+            const char *base = P.partials + int64_t(row) * P.S * P.partial_bytes;
+            float lm = -INFINITY;
+            for (int s = lane; s < P.S; s += kWave)
+                lm = fmaxf(lm, reinterpret_cast<const float *>(base + int64_t(s) * P.partial_bytes)[0]);
+            M = wave_max_f32(lm);
+            const float C = scale_ref(M);
+            float ls = 0.0f;
+            for (int s = lane; s < P.S; s += kWave) {
+                const float *r = reinterpret_cast<const float *>(base + int64_t(s) * P.partial_bytes);
+                ls += r[1] * __builtin_amdgcn_exp2f(scale_ref(r[0]) - C);
+            }
+            Ssum = wave_sum_f32(ls);
+            // keys: append with the same capacity/compaction rule as the stream
+            int cnt = 0;
+            uint64_t thk = 0, kth;
+            const int tot = P.S * P.k;
+            for (int e0 = 0; e0 < tot; e0 += kWave) {
+                if (cnt + kWave > kCap) {
+                    cnt = wave_select_topk<kCap / kWave>(cand, cnt, P.k, kth);
+                    thk = kth;
+                }
+                const int e = e0 + lane;
+                uint64_t key = 0;
+                if (e < tot) {
+                    const int s = e / P.k, j = e - s * P.k;
+                    key = reinterpret_cast<const uint64_t *>(base + int64_t(s) * P.partial_bytes + 16)[j];
+                }
+                const bool p = key != 0 && key > thk;
+                const uint64_t msk = __ballot(p);
+                if (p) cand[cnt + popc64(msk & lanemask_lt())] = key;
+                cnt += popc64(msk);
+                wave_sync();
+            }
+            nsel = wave_select_topk<kCap / kWave>(cand, cnt, P.k, kth);
+        }
+    }
+    // ---- finish the row (wave 0) ----
+    if (wv == 0) {
+        const bool badrow = (nsel < P.k) || !(Ssum == Ssum) || !(fabsf(M) <= kMaxAbsRowMax);
+        const int64_t o = int64_t(row) * P.k;
+        if (lane < P.k) {
+            if (badrow) {
+                P.topk_ids[o + lane] = -1;
+                P.topk_q[o + lane] = 0.0f;
+            } else {
+                const uint64_t key = cand[lane];
+                const float C = scale_ref(M);
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(topk_key_value(key), kLog2e, -C));
+                P.topk_ids[o + lane] = topk_key_token(key);
+                P.topk_q[o + lane] = e / Ssum;
+            }
+        }
+        if (lane == 0) {
+            const float C = scale_ref(M);
+            const float d = __builtin_fmaf(M, kLog2e, -C);   // rounding residual of C
+            P.row_max[row] = badrow ? 0.0f : M;
+            P.row_sum[row] = badrow ? 0.0f : Ssum * __builtin_amdgcn_exp2f(-d);
+            P.row_status[row] = badrow ? BASTION_Q_BAD_LOGITS : BASTION_Q_OK;
+        }
+    }
+    if (!arrive_last(P.query_ticket + q, uint32_t(P.b))) return;
+    tree_stage<R>(P, q, smem);
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch helpers (called from api.hip).
+// ---------------------------------------------------------------------------
+template <typename T, int U, int R>
+static hipError_t launch_one(const BuildParams &P, int smem, hipStream_t s) {
+    auto kern = build_trees_kernel<T, U, R>;
+    const int64_t grid = int64_t(P.B) * P.b * P.S;
+    hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), smem, s, P);
+    return hipGetLastError();
+}
+
+template <typename T, int U>
+static hipError_t launch_r(const BuildParams &P, int smem, hipStream_t s) {
+    const int slots = P.nmax + 1;   // frontier slots (parents 0..nmax)
+    if (slots <= 64) return launch_one<T, U, 1>(P, smem, s);
+    if (slots <= 128) return launch_one<T, U, 2>(P, smem, s);
+    if (slots <= 256) return launch_one<T, U, 4>(P, smem, s);
+    if (slots <= 512) return launch_one<T, U, 8>(P, smem, s);
+    return launch_one<T, U, 16>(P, smem, s);
+}
+
+}  // namespace bastion
+
+// entry used by api.hip
+hipError_t bastion_launch_build(const bastion::BuildParams &P, int dtype, hipStream_t s,
+                                int *smem_out) {
+    using namespace bastion;
+    constexpr int U = 4;
+    const int stream_smem = int(sizeof(WaveScratch<U>)) * kWavesPerBlock;
+    const int tree_smem = tree_layout(P.b, P.k, P.nmax).total;
+    const int smem = stream_smem > tree_smem ? stream_smem : tree_smem;
+    if (smem_out) *smem_out = smem;
+    if (dtype == BASTION_BF16) return launch_r<__bf16, U>(P, smem, s);
+    return launch_r<float, U>(P, smem, s);
+}

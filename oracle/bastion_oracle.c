@@ -220,7 +220,13 @@ void oracle_best_first(const int32_t *topk_ids, const float *topk_q,
                 if (row_status[q * b + p] != ORACLE_OK)
                     bad = 1;
         if (bad) {
-            pad_tree(q, 0, nmax, parent, depth, token, rho, ahat);
+            /* the tree is the root alone */
+            parent[o] = -1;
+            depth[o] = 0;
+            token[o] = -1;
+            rho[o] = 1.0f;
+            ahat[o] = 1.0;
+            pad_tree(q, 1, nmax, parent, depth, token, rho, ahat);
             n_nodes[q] = 0;
             qstatus[q] = ORACLE_BAD_LOGITS;
             continue;
@@ -578,7 +584,13 @@ void oracle_mixture_tree(const float *w, const int32_t *cand_count,
                 if (row_status[(int64_t)q * K * b + r] != ORACLE_OK)
                     bad = 1;
         if (bad) {
-            pad_tree(q, 0, nmax, parent, depth, token, rho, ahat);
+            /* the tree is the root alone */
+            parent[o] = -1;
+            depth[o] = 0;
+            token[o] = -1;
+            rho[o] = 1.0f;
+            ahat[o] = 1.0;
+            pad_tree(q, 1, nmax, parent, depth, token, rho, ahat);
             n_nodes[q] = 0;
             qstatus[q] = ORACLE_BAD_LOGITS;
             continue;
