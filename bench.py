@@ -1,0 +1,158 @@
+"""Benchmark of the tree-drafting hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload main]
+
+A step is one bastion_build_trees call (softmax + top-k over the vocabulary,
+best-first tree with A_hat, mask and position ids) over one batch of
+synthetic logits that is already resident in HBM.  Four distinct input
+batches rotate so that no step finds its logits in the 256 MB MALL.
+
+Prints one JSON line.  `value` is trees per second over the timed steps.
+`roofline` is the fused kernel's algorithmic bytes per launch (every logit
+read once plus every output written once) over its mean launch time,
+measured with HIP events recorded on the stream the kernel runs on.
+`cpu_baseline` times the CPU reference on the same batch (host copy).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+WORKLOAD_TEXT = {
+    "main": "B=64 queries x b=16 positions x V=151936 bf16 logits, k=8, fixed N=64",
+    "sweep": "B=256 x b=16 x V=128256 fp32 logits, k=4, online stop over N<=256",
+    "latency": "B=1 x b=16 x V=151936 bf16 logits, k=16, online stop over N<=128",
+    "tiny": "B=1 x b=4 x V=1024 fp32 logits, k=4, fixed N=32",
+}
+HBM_PEAK_GBS = 8000.0
+N_BUFFERS = 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="main", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                           "profiles", "traffic.json"))
+    return ap.parse_args()
+
+
+def out_bytes(out) -> int:
+    return int(sum(t.numel() * t.element_size() for t in out.values()))
+
+
+def cpu_baseline(x_host, wl, n_queries):
+    """The CPU reference on the first n_queries queries of the batch."""
+    from oracle import oracle
+    import numpy as np
+    sample = x_host[:n_queries]
+    t0 = time.perf_counter()
+    rows = oracle.softmax_topk(sample, k=wl.k)
+    tree = oracle.best_first(rows["topk_ids"], rows["topk_p"].astype(np.float32), nmax=wl.nmax,
+                             row_status=rows["row_status"])
+    oracle.tree_mask(tree["parent"], tree["n_nodes"])
+    dt = time.perf_counter() - t0
+    return dict(value=n_queries / dt, unit="trees/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"first {n_queries} of {wl.B} queries of the timed batch "
+                       f"({n_queries * wl.b} rows), float64 softmax+top-k, best-first tree, "
+                       f"mask; {dt:.2f} s"), rows
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards over queries with no exchange, so N GPUs run N copies.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from block_diffusion_tree_amd import binding, synth
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    binding.lib()
+    bufs = [synth.make_logits(wl, device=dev, seed=wl.seed + i) for i in range(N_BUFFERS)]
+    cost = None
+    if wl.online:
+        c, _ = synth.make_cost_table(wl.B, wl.nmax, seed=wl.seed, **synth.LATENCY_A100)
+        cost = torch.from_numpy(c).to(dev)
+    ws = binding.Workspace(dev)
+    outs = [binding.alloc_tree_out(wl.B, wl.b, wl.k, wl.nmax, dev) for _ in range(N_BUFFERS)]
+
+    def step(i):
+        binding.build_trees(bufs[i % N_BUFFERS], k=wl.k, nmax=wl.nmax, nmin=wl.nmin, cost=cost,
+                            out=outs[i % N_BUFFERS], ws=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+
+    ms_per_step = wall * 1e3 / args.steps
+    alg_bytes = wl.logit_bytes + out_bytes(outs[0])
+    mean_ms = float(launch_ms.mean())
+    achieved = alg_bytes / (mean_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            traffic = json.load(open(args.traffic_json)).get(args.workload)
+        except Exception:
+            traffic = None
+    line = {
+        "metric": "draft trees/sec + achieved HBM GB/s, B=64 b=16 V=151936 N<=64, 1 MI355X",
+        "value": wl.B / (ms_per_step * 1e-3),
+        "unit": "trees/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}",
+                   "logits_dtype": wl.dtype, "rotating_buffers": N_BUFFERS},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "build_trees_kernel", "alg_bytes_per_launch": alg_bytes,
+                     "launch_us_mean": mean_ms * 1e3,
+                     "launch_us_p50": float(np.median(launch_ms)) * 1e3,
+                     "launch_us_p10": float(np.percentile(launch_ms, 10)) * 1e3,
+                     "launch_us_p90": float(np.percentile(launch_ms, 90)) * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+        x_host = oracle.host_logits(bufs[0])
+        n_q = wl.B
+        base, rows = cpu_baseline(x_host, wl, n_q)
+        line["cpu_baseline"] = base
+        # the timed GPU outputs of buffer 0 agree with the reference sample
+        g_ids = outs[0]["topk_ids"][:n_q].cpu().numpy()
+        line["parity_sample"] = {"queries": n_q,
+                                 "topk_ids_exact": bool((g_ids == rows["topk_ids"]).all())}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

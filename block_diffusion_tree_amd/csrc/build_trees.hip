@@ -77,6 +77,7 @@ struct Streamer {
     int cnt;       // keys in ws->cand
     int nstage;
     int head;      // elements of the row before its first 16-byte aligned vector
+    bool booted;   // the first tile has set a threshold
 
     __device__ void compact() {
         uint64_t kth;
@@ -111,6 +112,8 @@ struct Streamer {
             wave_sync();
         }
         nstage = 0;
+        // keep the threshold close to the true k-th key seen so far
+        if (cnt >= 2 * k + 8) compact();
     }
 
     // Candidates that are single elements (the scalar tail of a row).
@@ -167,6 +170,16 @@ struct Streamer {
         sm.m = m_new;
         sm.c = c_new;
 
+        if (!booted) {
+            // first tile: the k-th largest lane maximum is a lower bound of
+            // the k-th largest element (k distinct elements reach it)
+            booted = true;
+            const float t0 = wave_kth_largest(tmax, k);
+            if (thk == 0 && t0 > thv) {
+                thv = t0;
+                thk = uint64_t(ord_f32(t0)) << 32;   // below every key of value t0
+            }
+        }
         bool pass[U];
         bool any = false;
 #pragma unroll
@@ -237,6 +250,7 @@ __device__ SegmentResult stream_segment(const BuildParams &P, const char *row, i
     st.cnt = 0;
     st.nstage = 0;
     st.head = head;
+    st.booted = false;
     LaneSoftmax sm{-INFINITY, scale_ref(-INFINITY), 0.0f};
 
     const int span = kThreads * U;
@@ -290,8 +304,8 @@ __device__ SegmentResult stream_segment(const BuildParams &P, const char *row, i
         sm.c = c_new;
         st.offer_scalar(ok, v, uint32_t(elem));
     }
-    // per-wave final selection
-    if (st.cnt > P.k || st.thk == 0) st.compact();
+    // at most 64 keys per wave go to the block merge
+    if (st.cnt > kWave) st.compact();
 
     // ---- block merge: softmax state ----
     __shared__ float red_m[kWavesPerBlock], red_s[kWavesPerBlock];
@@ -332,14 +346,25 @@ __device__ SegmentResult stream_segment(const BuildParams &P, const char *row, i
 }
 
 // ---------------------------------------------------------------------------
-// Arrival ticket: the last of `total` blocks to arrive gets true.  Every
-// thread fences its own stores before the count; the winner fences again
-// before reading what the others wrote.  The counter is reset to 0 for the
-// next call.
+// Cross-block hand-off.  Data that another block reads (segment records,
+// the rows' top-k, row status) is written and read with agent-scope atomic
+// accesses, which gfx950 performs coherently across XCDs (sc1), so no L2
+// write-back or invalidate is needed.  arrive_last: every thread waits for
+// its stores to complete, then one thread counts the block in; the last of
+// `total` blocks gets true.  The counter is reset to 0 for the next call.
 // ---------------------------------------------------------------------------
+template <typename V>
+__device__ __forceinline__ void st_agent(V *p, V v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename V>
+__device__ __forceinline__ V ld_agent(const V *p) {
+    return __hip_atomic_load(const_cast<V *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ bool arrive_last(uint32_t *ticket, uint32_t total) {
     __shared__ int flag;
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's stores are done
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t old = atomicAdd(ticket, 1u);
@@ -348,9 +373,7 @@ __device__ bool arrive_last(uint32_t *ticket, uint32_t total) {
         flag = last;
     }
     __syncthreads();
-    const bool last = flag != 0;
-    if (last) __threadfence();
-    return last;
+    return flag != 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -497,8 +520,8 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
     const int bk = P.b * P.k;
     const int64_t tk0 = int64_t(q) * bk;
     for (int e = tid; e < bk; e += kThreads) {
-        T.qtab[e] = P.topk_q[tk0 + e];
-        T.ttab[e] = P.topk_ids[tk0 + e];
+        T.qtab[e] = ld_agent(P.topk_q + tk0 + e);
+        T.ttab[e] = ld_agent(P.topk_ids + tk0 + e);
     }
     const bool online = P.cost != nullptr;
     if (online)
@@ -506,7 +529,8 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
             T.cost[e] = P.cost[int64_t(q) * P.cost_qstride + e];
     if (tid == 0) s_bad = 0;
     __syncthreads();
-    if (tid < P.b && P.row_status[int64_t(q) * P.b + tid] != BASTION_Q_OK) atomicOr(&s_bad, 1);
+    if (tid < P.b && ld_agent(P.row_status + int64_t(q) * P.b + tid) != BASTION_Q_OK)
+        atomicOr(&s_bad, 1);
     __syncthreads();
     const bool bad = s_bad != 0;
 
@@ -645,11 +669,13 @@ __global__ __launch_bounds__(kThreads, 4) void build_trees_kernel(BuildParams P)
         char *rec = P.partials + (int64_t(row) * P.S + seg) * P.partial_bytes;
         if (wv == 0) {
             if (lane == 0) {
-                reinterpret_cast<float *>(rec)[0] = M;
-                reinterpret_cast<float *>(rec)[1] = Ssum;
-                reinterpret_cast<int32_t *>(rec)[2] = nsel;
+                st_agent(reinterpret_cast<float *>(rec), M);
+                st_agent(reinterpret_cast<float *>(rec) + 1, Ssum);
+                st_agent(reinterpret_cast<int32_t *>(rec) + 2, nsel);
             }
-            if (lane < P.k) reinterpret_cast<uint64_t *>(rec + 16)[lane] = lane < nsel ? cand[lane] : 0;
+            if (lane < P.k)
+                st_agent(reinterpret_cast<uint64_t *>(rec + 16) + lane,
+                         lane < nsel ? cand[lane] : uint64_t(0));
         }
         if (!arrive_last(P.row_ticket + row, uint32_t(P.S))) return;
         // merge the S segment records of this row (wave 0)
@@ -657,13 +683,13 @@ __global__ __launch_bounds__(kThreads, 4) void build_trees_kernel(BuildParams P)
             const char *base = P.partials + int64_t(row) * P.S * P.partial_bytes;
             float lm = -INFINITY;
             for (int s = lane; s < P.S; s += kWave)
-                lm = fmaxf(lm, reinterpret_cast<const float *>(base + int64_t(s) * P.partial_bytes)[0]);
+                lm = fmaxf(lm, ld_agent(reinterpret_cast<const float *>(base + int64_t(s) * P.partial_bytes)));
             M = wave_max_f32(lm);
             const float C = scale_ref(M);
             float ls = 0.0f;
             for (int s = lane; s < P.S; s += kWave) {
                 const float *r = reinterpret_cast<const float *>(base + int64_t(s) * P.partial_bytes);
-                ls += r[1] * __builtin_amdgcn_exp2f(scale_ref(r[0]) - C);
+                ls += ld_agent(r + 1) * __builtin_amdgcn_exp2f(scale_ref(ld_agent(r)) - C);
             }
             Ssum = wave_sum_f32(ls);
             // keys: append with the same capacity/compaction rule as the stream
@@ -679,7 +705,7 @@ __global__ __launch_bounds__(kThreads, 4) void build_trees_kernel(BuildParams P)
                 uint64_t key = 0;
                 if (e < tot) {
                     const int s = e / P.k, j = e - s * P.k;
-                    key = reinterpret_cast<const uint64_t *>(base + int64_t(s) * P.partial_bytes + 16)[j];
+                    key = ld_agent(reinterpret_cast<const uint64_t *>(base + int64_t(s) * P.partial_bytes + 16) + j);
                 }
                 const bool p = key != 0 && key > thk;
                 const uint64_t msk = __ballot(p);
@@ -696,14 +722,14 @@ __global__ __launch_bounds__(kThreads, 4) void build_trees_kernel(BuildParams P)
         const int64_t o = int64_t(row) * P.k;
         if (lane < P.k) {
             if (badrow) {
-                P.topk_ids[o + lane] = -1;
-                P.topk_q[o + lane] = 0.0f;
+                st_agent(P.topk_ids + o + lane, int32_t(-1));
+                st_agent(P.topk_q + o + lane, 0.0f);
             } else {
                 const uint64_t key = cand[lane];
                 const float C = scale_ref(M);
                 const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(topk_key_value(key), kLog2e, -C));
-                P.topk_ids[o + lane] = topk_key_token(key);
-                P.topk_q[o + lane] = e / Ssum;
+                st_agent(P.topk_ids + o + lane, topk_key_token(key));
+                st_agent(P.topk_q + o + lane, e / Ssum);
             }
         }
         if (lane == 0) {
@@ -711,7 +737,7 @@ __global__ __launch_bounds__(kThreads, 4) void build_trees_kernel(BuildParams P)
             const float d = __builtin_fmaf(M, kLog2e, -C);   // rounding residual of C
             P.row_max[row] = badrow ? 0.0f : M;
             P.row_sum[row] = badrow ? 0.0f : Ssum * __builtin_amdgcn_exp2f(-d);
-            P.row_status[row] = badrow ? BASTION_Q_BAD_LOGITS : BASTION_Q_OK;
+            st_agent(P.row_status + row, int32_t(badrow ? BASTION_Q_BAD_LOGITS : BASTION_Q_OK));
         }
     }
     if (!arrive_last(P.query_ticket + q, uint32_t(P.b))) return;

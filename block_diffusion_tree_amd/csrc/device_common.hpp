@@ -8,7 +8,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/bastion.h"
+#include "bastion.h"
 
 namespace bastion {
 
@@ -94,33 +94,107 @@ __device__ __forceinline__ int tree_key_parent(uint64_t key) {
 }
 
 // ---------------------------------------------------------------------------
-// Wave reductions (all 64 lanes active).  Results are wave-uniform.
+// Wave reductions (all 64 lanes active), as butterflies on the gfx950
+// cross-lane paths: DPP quad permutes and row mirrors inside each 16-lane
+// row, then v_permlane16_swap / v_permlane32_swap across rows.  After each
+// step every lane of a group holds the group's value, so pairing a lane with
+// any lane of the partner group completes the step.  Results are
+// wave-uniform.
 // ---------------------------------------------------------------------------
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
+}
+
+// v paired with a lane of the other 16-lane row (16) / other half-wave (32):
+// both swap results together hold {own value, partner's value}.
+__device__ __forceinline__ void swap16(uint32_t v, uint32_t &a, uint32_t &b) {
+    auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    a = r[0];
+    b = r[1];
+}
+__device__ __forceinline__ void swap32(uint32_t v, uint32_t &a, uint32_t &b) {
+    auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    a = r[0];
+    b = r[1];
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+    return (uint64_t(dpp32<CTRL>(uint32_t(v >> 32))) << 32) | dpp32<CTRL>(uint32_t(v));
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint64_t o = __shfl_xor(v, off, kWave);
-        v = o > v ? o : v;
-    }
-    return v;
+    v = max_u64(v, dpp64<kDppXor1>(v));
+    v = max_u64(v, dpp64<kDppXor2>(v));
+    v = max_u64(v, dpp64<kDppHalfMirror>(v));
+    v = max_u64(v, dpp64<kDppMirror>(v));
+    uint32_t h0, h1, l0, l1;
+    swap16(uint32_t(v >> 32), h0, h1);
+    swap16(uint32_t(v), l0, l1);
+    v = max_u64((uint64_t(h0) << 32) | l0, (uint64_t(h1) << 32) | l1);
+    swap32(uint32_t(v >> 32), h0, h1);
+    swap32(uint32_t(v), l0, l1);
+    return max_u64((uint64_t(h0) << 32) | l0, (uint64_t(h1) << 32) | l1);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp32<kDppXor1>(v));
+    v = max(v, dpp32<kDppXor2>(v));
+    v = max(v, dpp32<kDppHalfMirror>(v));
+    v = max(v, dpp32<kDppMirror>(v));
+    uint32_t a, b;
+    swap16(v, a, b);
+    v = max(a, b);
+    swap32(v, a, b);
+    return max(a, b);
 }
 
 __device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-    return v;
+    v = fmaxf(v, __uint_as_float(dpp32<kDppXor1>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp32<kDppXor2>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp32<kDppHalfMirror>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp32<kDppMirror>(__float_as_uint(v))));
+    uint32_t a, b;
+    swap16(__float_as_uint(v), a, b);
+    v = fmaxf(__uint_as_float(a), __uint_as_float(b));
+    swap32(__float_as_uint(v), a, b);
+    return fmaxf(__uint_as_float(a), __uint_as_float(b));
 }
 
+// Sum: IEEE addition is commutative, so the two lanes of each pair compute
+// bit-identical partial sums and every lane ends with the same result.
 __device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
+    v += __uint_as_float(dpp32<kDppXor1>(__float_as_uint(v)));
+    v += __uint_as_float(dpp32<kDppXor2>(__float_as_uint(v)));
+    v += __uint_as_float(dpp32<kDppHalfMirror>(__float_as_uint(v)));
+    v += __uint_as_float(dpp32<kDppMirror>(__float_as_uint(v)));
+    uint32_t a, b;
+    swap16(__float_as_uint(v), a, b);
+    v = __uint_as_float(a) + __uint_as_float(b);
+    swap32(__float_as_uint(v), a, b);
+    return __uint_as_float(a) + __uint_as_float(b);
 }
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
+// k-th largest of the 64 lane values, ties counted (-inf if fewer than k
+// values above -inf).  At most k wave-max rounds.
+__device__ __forceinline__ float wave_kth_largest(float v, int k) {
+    int found = 0;
+    for (int r = 0; r < k; ++r) {
+        const float m = wave_max_f32(v);
+        if (!(m > -INFINITY)) break;
+        found += popc64(__ballot(v == m));
+        if (found >= k) return m;
+        v = (v == m) ? -INFINITY : v;
+    }
+    return -INFINITY;
 }
 
 // Scale reference of the online softmax: c = fl(m * log2 e), kept finite so

@@ -64,6 +64,13 @@
 
 int oracle_abi_version(void) { return 1; }
 
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+#else
+int oracle_num_threads(void) { return 1; }
+#endif
+
 /* bf16 is the upper half of an IEEE binary32. */
 static double logit_at(const void *base, int dtype, int64_t idx)
 {

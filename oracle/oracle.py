@@ -52,6 +52,7 @@ I32, I64, F64 = C.c_int, C.c_int64, C.c_double
 
 def _declare(L):
     L.oracle_abi_version.restype = I32
+    L.oracle_num_threads.restype = I32
     L.oracle_softmax_topk.argtypes = [P, I32, I64, I32, I64, I32, P, P, P, P, P]
     L.oracle_best_first.argtypes = [P, P, P, I32, I32, I32, I32, I32, P, I64, F64,
                                     P, P, P, P, P, P, P]
@@ -67,6 +68,10 @@ def _declare(L):
               "oracle_tree_mask", "oracle_accept", "oracle_mixture",
               "oracle_qdep_sequences", "oracle_mixture_tree"):
         getattr(L, f).restype = None
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
 
 
 def _p(a):
