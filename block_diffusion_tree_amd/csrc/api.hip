@@ -48,11 +48,11 @@ struct Layout {
     int S;
 };
 
-// Segments per row: enough blocks to cover the machine (256 CUs, several
-// blocks each) without making a segment shorter than one 16-byte load per
-// thread.  BASTION_SEGMENTS overrides (tuning).
+// Segments per row: enough blocks to cover the machine (256 CUs, four
+// resident blocks each) without making a segment shorter than one 16-byte
+// load per thread.  BASTION_SEGMENTS overrides (tuning).
 int plan_segments(int64_t rows, int V, int dtype) {
-    int S = int((2048 + rows - 1) / rows);
+    int S = int((1024 + rows - 1) / rows);
     const char *env = getenv("BASTION_SEGMENTS");
     if (env && atoi(env) > 0) S = atoi(env);
     const int64_t row_bytes = int64_t(V) * esize(dtype);

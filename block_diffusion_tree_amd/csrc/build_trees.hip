@@ -377,10 +377,21 @@ __device__ bool arrive_last(uint32_t *ticket, uint32_t total) {
 }
 
 // ---------------------------------------------------------------------------
-// Tree stage.  LDS layout (byte offsets computed by tree_layout()).
+// Tree stage: one wave builds the best-first tree of one query.
+//
+// The frontier holds one key per popped node p (slot p): p's best child not
+// popped yet.  Children of a node are offered in rank order (rank j = j-th
+// candidate of the position), which is their pop order unless a rounding tie
+// of rho puts a larger token first; positions where that can happen, or
+// products that leave the normal float range, switch the node to an exact
+// path (argmax over its remaining children).  Everything a pop touches lives
+// in registers: slot arrays and candidate tables are spread over lanes and
+// accessed with v_readlane / v_writelane, so a pop has no LDS round trip.
+// LDS keeps the node records for the output and the tables for the exact
+// path.
 // ---------------------------------------------------------------------------
 struct TreeLayout {
-    int qtab, ttab, par, dep, tok, rho, nxt, popm, slow, ahat, cost, total;
+    int qtab, ttab, par, dep, tok, rho, popm, ahat, cost, total;
 };
 
 __host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
@@ -395,164 +406,270 @@ __host__ __device__ inline TreeLayout tree_layout(int b, int k, int nmax) {
     L.dep = o;  o = align16(o + 4 * nn);
     L.tok = o;  o = align16(o + 4 * nn);
     L.rho = o;  o = align16(o + 4 * nn);
-    L.nxt = o;  o = align16(o + 4 * nn);
     L.popm = o; o = align16(o + 4 * nn);
-    L.slow = o; o = align16(o + 4 * nn);
     L.ahat = o; o = align16(o + 8 * nn);
     L.cost = o; o = align16(o + 8 * nn);
     L.total = o;
     return L;
 }
 
-// The frontier holds one key per popped node p (slot p): p's best child
-// that has not been popped yet.  Slot p lives in lane p % 64 of register
-// p / 64.
-template <int R>
-struct Frontier {
-    uint64_t key[R];
+// Element s of a wave-distributed array lives in lane s % 64 of register
+// s / 64; s must be wave-uniform.
+template <int G>
+struct LaneArray {
+    uint32_t r[G];
+    __device__ __forceinline__ void fill(uint32_t v) {
+#pragma unroll
+        for (int i = 0; i < G; ++i) r[i] = v;
+    }
+    // every register is touched so that the array never becomes a
+    // dynamically indexed (scratch) object
+    __device__ __forceinline__ uint32_t get(int s) const {
+        const int g = s >> 6, l = s & 63;
+        uint32_t v = 0;
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const uint32_t t = uint32_t(__builtin_amdgcn_readlane(int(r[i]), l));
+            v = (g == i) ? t : v;
+        }
+        return v;
+    }
+    __device__ __forceinline__ void set(int s, uint32_t v) {
+        const int g = s >> 6;
+        const bool mine = lane_id() == (s & 63);
+#pragma unroll
+        for (int i = 0; i < G; ++i) r[i] = (mine && g == i) ? v : r[i];
+    }
+};
+
+constexpr uint32_t kSlowNode = 256u;   // cursor flag: exact sibling order path
+constexpr int kDppWaveShl1 = 0x130;     // lane i <- lane i+1 (lane 63 <- old)
+constexpr int kDppWaveShr1 = 0x138;     // lane i <- lane i-1 (lane 0 <- old)
+
+// Frontier kept sorted in descending key order: element i (lane i % 64 of
+// register i / 64) is the i-th best key, unused elements are 0.  The best
+// key is lane 0 of register 0; removing it is one wave shift per register,
+// inserting is a compare + ballot + popcount for the position and one
+// wave shift per register.
+template <int G>
+struct SortedFrontier {
+    uint32_t h[G], l[G];
     __device__ __forceinline__ void clear() {
 #pragma unroll
-        for (int r = 0; r < R; ++r) key[r] = 0;
+        for (int g = 0; g < G; ++g) h[g] = l[g] = 0;
     }
-    __device__ __forceinline__ void set(int slot, uint64_t v) {
+    __device__ __forceinline__ uint64_t front() const {
+        return (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(h[0])))) << 32) |
+               uint32_t(__builtin_amdgcn_readfirstlane(int(l[0])));
+    }
+    __device__ __forceinline__ void pop_front() {
+        int ch = 0, cl = 0;   // lane 0 of the next register
+#pragma unroll
+        for (int g = G - 1; g >= 0; --g) {
+            const int nh = __builtin_amdgcn_readlane(int(h[g]), 0);
+            const int nl = __builtin_amdgcn_readlane(int(l[g]), 0);
+            h[g] = uint32_t(__builtin_amdgcn_update_dpp(ch, int(h[g]), kDppWaveShl1, 0xF, 0xF, false));
+            l[g] = uint32_t(__builtin_amdgcn_update_dpp(cl, int(l[g]), kDppWaveShl1, 0xF, 0xF, false));
+            ch = nh;
+            cl = nl;
+        }
+    }
+    __device__ __forceinline__ void insert(uint64_t key) {
+        const uint32_t kh = uint32_t(key >> 32), kl = uint32_t(key);
+        int pos = 0;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const bool gt = h[g] > kh || (h[g] == kh && l[g] > kl);
+            pos += popc64(__ballot(gt));
+        }
         const int lane = lane_id();
+        int ch = 0, cl = 0;   // lane 63 of the previous register
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-            if (slot == r * kWave + lane) key[r] = v;
-    }
-    __device__ __forceinline__ uint64_t best() const {
-        uint64_t m = key[0];
-#pragma unroll
-        for (int r = 1; r < R; ++r) m = key[r] > m ? key[r] : m;
-        return wave_max_u64(m);
+        for (int g = 0; g < G; ++g) {
+            const int lh = __builtin_amdgcn_readlane(int(h[g]), 63);
+            const int ll = __builtin_amdgcn_readlane(int(l[g]), 63);
+            const uint32_t sh = uint32_t(__builtin_amdgcn_update_dpp(ch, int(h[g]), kDppWaveShr1, 0xF, 0xF, false));
+            const uint32_t sl = uint32_t(__builtin_amdgcn_update_dpp(cl, int(l[g]), kDppWaveShr1, 0xF, 0xF, false));
+            const int idx = g * kWave + lane;
+            h[g] = idx > pos ? sh : (idx == pos ? kh : h[g]);
+            l[g] = idx > pos ? sl : (idx == pos ? kl : l[g]);
+            ch = lh;
+            cl = ll;
+        }
     }
 };
 
-struct TreeCtx {
-    float *qtab;
-    int32_t *ttab, *par, *dep, *tok, *nxt, *slow;
-    uint32_t *popm;
-    float *rho;
-    double *ahat, *cost;
-    int b, k;
-};
+template <int G>
+struct PopState {
+    SortedFrontier<G> F;     // every offered key but `pending`
+    uint64_t pending;        // one more offered key (0: none)
+    LaneArray<G> nrho;       // float bits of each popped node's rho
+    LaneArray<G> ncur;       // rank of the child on offer (| kSlowNode)
+    LaneArray<G> qt, tt;     // candidate tables: entry pos * k + j
+    uint32_t qf, tf, ql, sf; // lane = position: q / token of rank 0, q of
+                             // rank k-1, rank order is safe at this position
+    const float *qtab;       // LDS copies of the tables (exact path)
+    const int32_t *ttab;
+    uint32_t *popm;          // LDS: popped-rank mask of exact-path nodes
+    int k;
 
-// Offer node n's first child (in pop order among its siblings); node n has
-// rho rn and depth dn < b.  Siblings are normally already in pop order by
-// rank j (q non-increasing); if rounding ties put a larger token first, the
-// node is marked slow and its children are served by argmax over ranks.
-__device__ __forceinline__ uint64_t first_child(const TreeCtx &T, int n, float rn, int dn) {
-    const int lane = lane_id();
-    const bool in = lane < T.k;
-    uint64_t key = 0;
-    if (in) {
-        const float pr = __fmul_rn(rn, T.qtab[dn * T.k + lane]);
-        key = tree_key(pr, dn + 1, T.ttab[dn * T.k + lane], n);
-    }
-    const uint64_t nextk = __shfl_down(key, 1, kWave);
-    const bool bad = (lane + 1 < T.k) && !(key > nextk);
-    const bool slow = __ballot(bad) != 0;
-    uint64_t first;
-    int rank;
-    if (!slow) {
-        first = __shfl(key, 0, kWave);
-        rank = 0;
-    } else {
-        first = wave_max_u64(key);
-        rank = __ffsll((unsigned long long)__ballot(in && key == first)) - 1;
-    }
-    if (lane == 0) {
-        T.nxt[n] = rank;
-        T.slow[n] = slow ? 1 : 0;
-        T.popm[n] = 0u;
-    }
-    return first;
-}
-
-// Node p's offered child was just popped; return p's next offer (0: none).
-__device__ __forceinline__ uint64_t next_child(const TreeCtx &T, int p, int dchild) {
-    const int lane = lane_id();
-    const float rp = T.rho[p];
-    const int pos = dchild - 1;
-    const int cur = T.nxt[p];
-    if (!T.slow[p]) {
-        const int c = cur + 1;
+    // exact path: best child of node n (rho rn, depth dn + 1 children at
+    // position dn) among ranks not in `popped`; returns key, sets rank
+    __device__ __forceinline__ uint64_t exact_child(int n, float rn, int dn, uint32_t popped,
+                                                    int &rank) {
+        const int lane = lane_id();
+        const bool in = lane < k && !((popped >> lane) & 1u);
         uint64_t key = 0;
-        if (c < T.k) key = tree_key(__fmul_rn(rp, T.qtab[pos * T.k + c]), dchild,
-                                    T.ttab[pos * T.k + c], p);
-        if (lane == 0) T.nxt[p] = c;
+        if (in) key = tree_key(__fmul_rn(rn, qtab[dn * k + lane]), dn + 1, ttab[dn * k + lane], n);
+        const uint64_t best = wave_max_u64(key);
+        rank = best ? __ffsll((unsigned long long)__ballot(in && key == best)) - 1 : 0;
+        return best;
+    }
+
+    // node n (rho rn, depth dn < b) joins the tree: key of its first child
+    __device__ __forceinline__ uint64_t first_child(int n, float rn, int dn) {
+        const float q0 = __uint_as_float(uint32_t(__builtin_amdgcn_readlane(int(qf), dn)));
+        const float qk = __uint_as_float(uint32_t(__builtin_amdgcn_readlane(int(ql), dn)));
+        const uint32_t safe = uint32_t(__builtin_amdgcn_readlane(int(sf), dn));
+        uint64_t key;
+        uint32_t cur;
+        if (safe && __fmul_rn(rn, qk) >= 0x1p-125f) {
+            key = tree_key(__fmul_rn(rn, q0), dn + 1, __builtin_amdgcn_readlane(int(tf), dn), n);
+            cur = 0;
+        } else {
+            int rank;
+            key = exact_child(n, rn, dn, 0u, rank);
+            if (lane_id() == 0) popm[n] = 0u;
+            cur = uint32_t(rank) | kSlowNode;
+        }
+        nrho.set(n, __float_as_uint(rn));
+        ncur.set(n, cur);
         return key;
     }
-    const uint32_t popped = T.popm[p] | (1u << cur);
-    const bool in = lane < T.k && !((popped >> lane) & 1u);
-    uint64_t key = 0;
-    if (in) key = tree_key(__fmul_rn(rp, T.qtab[pos * T.k + lane]), dchild,
-                           T.ttab[pos * T.k + lane], p);
-    const uint64_t best = wave_max_u64(key);
-    const int rank = best ? __ffsll((unsigned long long)__ballot(in && key == best)) - 1 : 0;
-    if (lane == 0) {
-        T.popm[p] = popped;
-        T.nxt[p] = rank;
-    }
-    return best;
-}
 
-template <int R>
+    // the child on offer at node p (at depth d) was popped: key of the next
+    __device__ __forceinline__ uint64_t next_child(int p, int d) {
+        const uint32_t cur = ncur.get(p);
+        const float rp = __uint_as_float(nrho.get(p));
+        uint64_t key = 0;
+        if (!(cur & kSlowNode)) {
+            const int c = int(cur) + 1;
+            if (c < k) {
+                const int e = (d - 1) * k + c;
+                key = tree_key(__fmul_rn(rp, __uint_as_float(qt.get(e))), d, int(tt.get(e)), p);
+            }
+            ncur.set(p, uint32_t(c));
+        } else {
+            const uint32_t popped = popm[p] | (1u << (cur & 255u));
+            int rank;
+            key = exact_child(p, rp, d - 1, popped, rank);
+            if (lane_id() == 0) popm[p] = popped;
+            ncur.set(p, uint32_t(rank) | kSlowNode);
+        }
+        return key;
+    }
+
+    // take the best offered key (0 when none is left)
+    __device__ __forceinline__ uint64_t pop() {
+        const uint64_t fr = F.front();
+        if (pending > fr) {
+            const uint64_t t = pending;
+            pending = 0;
+            return t;
+        }
+        if (fr) F.pop_front();
+        return fr;
+    }
+
+    // new offers: the best of (pending, a, c) stays pending, the rest go to
+    // the sorted array
+    __device__ __forceinline__ void offer(uint64_t a, uint64_t c) {
+        uint64_t x = pending, y = a, z = c;
+        if (y > x) { const uint64_t t = x; x = y; y = t; }
+        if (z > x) { const uint64_t t = x; x = z; z = t; }
+        pending = x;
+        if (y) F.insert(y);
+        if (z) F.insert(z);
+    }
+};
+
+template <int G>
 __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const TreeLayout L = tree_layout(P.b, P.k, P.nmax);
-    TreeCtx T;
-    T.qtab = reinterpret_cast<float *>(smem + L.qtab);
-    T.ttab = reinterpret_cast<int32_t *>(smem + L.ttab);
-    T.par = reinterpret_cast<int32_t *>(smem + L.par);
-    T.dep = reinterpret_cast<int32_t *>(smem + L.dep);
-    T.tok = reinterpret_cast<int32_t *>(smem + L.tok);
-    T.rho = reinterpret_cast<float *>(smem + L.rho);
-    T.nxt = reinterpret_cast<int32_t *>(smem + L.nxt);
-    T.popm = reinterpret_cast<uint32_t *>(smem + L.popm);
-    T.slow = reinterpret_cast<int32_t *>(smem + L.slow);
-    T.ahat = reinterpret_cast<double *>(smem + L.ahat);
-    T.cost = reinterpret_cast<double *>(smem + L.cost);
-    T.b = P.b;
-    T.k = P.k;
+    float *qtab = reinterpret_cast<float *>(smem + L.qtab);
+    int32_t *ttab = reinterpret_cast<int32_t *>(smem + L.ttab);
+    int32_t *par = reinterpret_cast<int32_t *>(smem + L.par);
+    int32_t *dep = reinterpret_cast<int32_t *>(smem + L.dep);
+    int32_t *tok = reinterpret_cast<int32_t *>(smem + L.tok);
+    float *rho = reinterpret_cast<float *>(smem + L.rho);
+    uint32_t *popm = reinterpret_cast<uint32_t *>(smem + L.popm);
+    double *ahat = reinterpret_cast<double *>(smem + L.ahat);
+    double *cost = reinterpret_cast<double *>(smem + L.cost);
     __shared__ int s_bad, s_nstar, s_status;
+    const int b = P.b, k = P.k, bk = b * k;
 
-    const int bk = P.b * P.k;
     const int64_t tk0 = int64_t(q) * bk;
     for (int e = tid; e < bk; e += kThreads) {
-        T.qtab[e] = ld_agent(P.topk_q + tk0 + e);
-        T.ttab[e] = ld_agent(P.topk_ids + tk0 + e);
+        qtab[e] = ld_agent(P.topk_q + tk0 + e);
+        ttab[e] = ld_agent(P.topk_ids + tk0 + e);
     }
     const bool online = P.cost != nullptr;
     if (online)
         for (int e = tid; e <= P.nmax; e += kThreads)
-            T.cost[e] = P.cost[int64_t(q) * P.cost_qstride + e];
+            cost[e] = P.cost[int64_t(q) * P.cost_qstride + e];
     if (tid == 0) s_bad = 0;
     __syncthreads();
-    if (tid < P.b && ld_agent(P.row_status + int64_t(q) * P.b + tid) != BASTION_Q_OK)
+    if (tid < b && ld_agent(P.row_status + int64_t(q) * b + tid) != BASTION_Q_OK)
         atomicOr(&s_bad, 1);
     __syncthreads();
     const bool bad = s_bad != 0;
 
     if (!bad && wv == 0) {
-        Frontier<R> F;
-        F.clear();
-        // root
-        if (lane == 0) {
-            T.par[0] = -1;
-            T.dep[0] = 0;
-            T.tok[0] = -1;
-            T.rho[0] = 1.0f;
-            T.ahat[0] = 1.0;
+        PopState<G> S;
+        S.qtab = qtab;
+        S.ttab = ttab;
+        S.popm = popm;
+        S.k = k;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int e = lane + kWave * g;
+            S.qt.r[g] = e < bk ? __float_as_uint(qtab[e]) : 0u;
+            S.tt.r[g] = e < bk ? uint32_t(ttab[e]) : 0u;
         }
-        wave_sync();
-        F.set(0, first_child(T, 0, 1.0f, 0));
-        wave_sync();
+        S.qf = S.tf = S.ql = S.sf = 0;
+        if (lane < b) {
+            const int o = lane * k;
+            S.qf = __float_as_uint(qtab[o]);
+            S.tf = uint32_t(ttab[o]);
+            S.ql = __float_as_uint(qtab[o + k - 1]);
+            // rank order is the pop order at this position for every parent
+            // whose products stay normal, unless two neighbours are within
+            // 2^-22 of each other with the larger token first
+            uint32_t safe = 1;
+            for (int j = 0; j + 1 < k; ++j) {
+                const double a = qtab[o + j], c = qtab[o + j + 1];
+                if (ttab[o + j] > ttab[o + j + 1] && a < c * (1.0 + 0x1p-22)) safe = 0;
+            }
+            S.sf = safe;
+        }
+        S.F.clear();
+        S.pending = 0;
+        S.nrho.fill(0);
+        S.ncur.fill(0);
+        if (lane == 0) {
+            par[0] = -1;
+            dep[0] = 0;
+            tok[0] = -1;
+            rho[0] = 1.0f;
+            ahat[0] = 1.0;
+        }
+        S.offer(S.first_child(0, 1.0f, 0), 0);
         int count = 0, nstar = -1, status = BASTION_Q_OK;
         double ah = 1.0;
-        double s_prev = online ? (1.0 * P.l_ar) / T.cost[0] : 0.0;
+        double s_prev = online ? (1.0 * P.l_ar) / cost[0] : 0.0;
         while (true) {
-            const uint64_t top = F.best();
+            const uint64_t top = S.pop();
             if (top == 0) {
                 nstar = count;
                 status = count < P.nmax ? BASTION_Q_EXHAUSTED : BASTION_Q_OK;
@@ -565,7 +682,7 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
             const int n = count + 1;
             const double ah_n = ah + double(r);
             if (online) {
-                const double s_n = (ah_n * P.l_ar) / T.cost[n];
+                const double s_n = (ah_n * P.l_ar) / cost[n];
                 if (n - 1 >= P.nmin && s_n < s_prev) {
                     nstar = n - 1;
                     break;
@@ -575,24 +692,19 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
             count = n;
             ah = ah_n;
             if (lane == 0) {
-                T.par[n] = p;
-                T.dep[n] = d;
-                T.tok[n] = tkn;
-                T.rho[n] = r;
-                T.ahat[n] = ah_n;
+                par[n] = p;
+                dep[n] = d;
+                tok[n] = tkn;
+                rho[n] = r;
+                ahat[n] = ah_n;
             }
-            wave_sync();
-            const uint64_t np = next_child(T, p, d);
-            wave_sync();
-            F.set(p, np);
             if (count == P.nmax) {
                 nstar = count;
                 break;
             }
-            if (d < P.b) {
-                F.set(n, first_child(T, n, r, d));
-                wave_sync();
-            }
+            const uint64_t sib = S.next_child(p, d);
+            const uint64_t kid = d < b ? S.first_child(n, r, d) : 0;
+            S.offer(sib, kid);
         }
         if (lane == 0) {
             s_nstar = nstar;
@@ -606,11 +718,11 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
     const int64_t o = int64_t(q) * W1;
     for (int i = tid; i < W1; i += kThreads) {
         const bool v = i <= nstar && !bad;
-        P.parent[o + i] = v ? (i == 0 ? -1 : T.par[i]) : -1;
-        P.depth[o + i] = v ? (i == 0 ? 0 : T.dep[i]) : -1;
-        P.token[o + i] = v ? (i == 0 ? -1 : T.tok[i]) : -1;
-        P.rho[o + i] = v ? (i == 0 ? 1.0f : T.rho[i]) : 0.0f;
-        P.ahat[o + i] = v ? (i == 0 ? 1.0 : T.ahat[i]) : 0.0;
+        P.parent[o + i] = v ? (i == 0 ? -1 : par[i]) : -1;
+        P.depth[o + i] = v ? (i == 0 ? 0 : dep[i]) : -1;
+        P.token[o + i] = v ? (i == 0 ? -1 : tok[i]) : -1;
+        P.rho[o + i] = v ? (i == 0 ? 1.0f : rho[i]) : 0.0f;
+        P.ahat[o + i] = v ? (i == 0 ? 1.0 : ahat[i]) : 0.0;
     }
     if (bad && tid == 0) {
         P.parent[o] = -1;
@@ -633,8 +745,8 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
             if (i <= nstar) {
                 int j = i;
                 if (j / 32 == w) bits |= 1u << (j & 31);
-                while (j > 0 && steps < P.b) {
-                    j = T.par[j];
+                while (j > 0 && steps < b) {
+                    j = par[j];
                     ++steps;
                     if (j / 32 == w) bits |= 1u << (j & 31);
                 }
@@ -651,7 +763,7 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
 constexpr int partial_bytes(int k) { return 16 + 8 * k; }
 
 template <typename T, int U, int R>
-__global__ __launch_bounds__(kThreads, 4) void build_trees_kernel(BuildParams P) {
+__global__ __launch_bounds__(kThreads, (R >= 16 ? 2 : 4)) void build_trees_kernel(BuildParams P) {
     extern __shared__ __align__(16) char smem[];
     const int row = blockIdx.x / P.S;
     const int seg = blockIdx.x - row * P.S;
@@ -757,7 +869,8 @@ static hipError_t launch_one(const BuildParams &P, int smem, hipStream_t s) {
 
 template <typename T, int U>
 static hipError_t launch_r(const BuildParams &P, int smem, hipStream_t s) {
-    const int slots = P.nmax + 1;   // frontier slots (parents 0..nmax)
+    // lane arrays must hold nmax + 1 slots and b * k table entries
+    const int slots = (P.nmax + 1) > (P.b * P.k) ? (P.nmax + 1) : (P.b * P.k);
     if (slots <= 64) return launch_one<T, U, 1>(P, smem, s);
     if (slots <= 128) return launch_one<T, U, 2>(P, smem, s);
     if (slots <= 256) return launch_one<T, U, 4>(P, smem, s);
