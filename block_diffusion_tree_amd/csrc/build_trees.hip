@@ -14,6 +14,7 @@
 // Nothing waits on another block, so the grid needs no co-residency.
 #include "device_common.hpp"
 #include "build_params.hpp"
+#include "tree_rounds.hpp"
 
 namespace bastion {
 
@@ -377,24 +378,20 @@ __device__ bool arrive_last(uint32_t *ticket, uint32_t total) {
 }
 
 // ---------------------------------------------------------------------------
-// Tree stage: one wave builds the best-first tree of one query.
-//
-// The frontier holds one key per popped node p (slot p): p's best child not
-// popped yet.  Children of a node are offered in rank order (rank j = j-th
-// candidate of the position), which is their pop order unless a rounding tie
-// of rho puts a larger token first; positions where that can happen, or
-// products that leave the normal float range, switch the node to an exact
-// path (argmax over its remaining children).  Everything a pop touches lives
-// in registers: slot arrays and candidate tables are spread over lanes and
-// accessed with v_readlane / v_writelane, so a pop has no LDS round trip.
-// LDS keeps the node records for the output and the tables for the exact
-// path.
+// Tree stage (one block per query, the last one to finish a row of it): the
+// level-synchronous best-first build of tree_rounds.hpp, parent resolution,
+// A_hat, the online stop and the outputs.
 // ---------------------------------------------------------------------------
-struct TreeLayout {
-    int qtab, ttab, par, dep, tok, rho, popm, ahat, cost, total;
-};
-
 __host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
+
+__host__ __device__ inline int tree_regs(int nmax) {
+    const int need = (nmax + kWave - 1) / kWave;
+    return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
+}
+
+struct TreeLayout {
+    int qtab, ttab, col, par, dep, tok, rho, ahat, cost, map, base, total;
+};
 
 __host__ __device__ inline TreeLayout tree_layout(int b, int k, int nmax) {
     TreeLayout L;
@@ -402,222 +399,47 @@ __host__ __device__ inline TreeLayout tree_layout(int b, int k, int nmax) {
     int o = 0;
     L.qtab = o; o = align16(o + 4 * b * k);
     L.ttab = o; o = align16(o + 4 * b * k);
+    L.col = o;  o = align16(o + 8 * kWave * tree_regs(nmax));
     L.par = o;  o = align16(o + 4 * nn);
     L.dep = o;  o = align16(o + 4 * nn);
     L.tok = o;  o = align16(o + 4 * nn);
     L.rho = o;  o = align16(o + 4 * nn);
-    L.popm = o; o = align16(o + 4 * nn);
     L.ahat = o; o = align16(o + 8 * nn);
     L.cost = o; o = align16(o + 8 * nn);
+    L.map = o;  o = align16(o + 4 * nn);
+    L.base = o; o = align16(o + 4 * 40);
     L.total = o;
     return L;
 }
 
-// Element s of a wave-distributed array lives in lane s % 64 of register
-// s / 64; s must be wave-uniform.
-template <int G>
-struct LaneArray {
-    uint32_t r[G];
-    __device__ __forceinline__ void fill(uint32_t v) {
-#pragma unroll
-        for (int i = 0; i < G; ++i) r[i] = v;
-    }
-    // every register is touched so that the array never becomes a
-    // dynamically indexed (scratch) object
-    __device__ __forceinline__ uint32_t get(int s) const {
-        const int g = s >> 6, l = s & 63;
-        uint32_t v = 0;
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            const uint32_t t = uint32_t(__builtin_amdgcn_readlane(int(r[i]), l));
-            v = (g == i) ? t : v;
-        }
-        return v;
-    }
-    __device__ __forceinline__ void set(int s, uint32_t v) {
-        const int g = s >> 6;
-        const bool mine = lane_id() == (s & 63);
-#pragma unroll
-        for (int i = 0; i < G; ++i) r[i] = (mine && g == i) ? v : r[i];
-    }
-};
-
-constexpr uint32_t kSlowNode = 256u;   // cursor flag: exact sibling order path
-constexpr int kDppWaveShl1 = 0x130;     // lane i <- lane i+1 (lane 63 <- old)
-constexpr int kDppWaveShr1 = 0x138;     // lane i <- lane i-1 (lane 0 <- old)
-
-// Frontier kept sorted in descending key order: element i (lane i % 64 of
-// register i / 64) is the i-th best key, unused elements are 0.  The best
-// key is lane 0 of register 0; removing it is one wave shift per register,
-// inserting is a compare + ballot + popcount for the position and one
-// wave shift per register.
-template <int G>
-struct SortedFrontier {
-    uint32_t h[G], l[G];
-    __device__ __forceinline__ void clear() {
-#pragma unroll
-        for (int g = 0; g < G; ++g) h[g] = l[g] = 0;
-    }
-    __device__ __forceinline__ uint64_t front() const {
-        return (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(h[0])))) << 32) |
-               uint32_t(__builtin_amdgcn_readfirstlane(int(l[0])));
-    }
-    __device__ __forceinline__ void pop_front() {
-        int ch = 0, cl = 0;   // lane 0 of the next register
-#pragma unroll
-        for (int g = G - 1; g >= 0; --g) {
-            const int nh = __builtin_amdgcn_readlane(int(h[g]), 0);
-            const int nl = __builtin_amdgcn_readlane(int(l[g]), 0);
-            h[g] = uint32_t(__builtin_amdgcn_update_dpp(ch, int(h[g]), kDppWaveShl1, 0xF, 0xF, false));
-            l[g] = uint32_t(__builtin_amdgcn_update_dpp(cl, int(l[g]), kDppWaveShl1, 0xF, 0xF, false));
-            ch = nh;
-            cl = nl;
-        }
-    }
-    __device__ __forceinline__ void insert(uint64_t key) {
-        const uint32_t kh = uint32_t(key >> 32), kl = uint32_t(key);
-        int pos = 0;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const bool gt = h[g] > kh || (h[g] == kh && l[g] > kl);
-            pos += popc64(__ballot(gt));
-        }
-        const int lane = lane_id();
-        int ch = 0, cl = 0;   // lane 63 of the previous register
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int lh = __builtin_amdgcn_readlane(int(h[g]), 63);
-            const int ll = __builtin_amdgcn_readlane(int(l[g]), 63);
-            const uint32_t sh = uint32_t(__builtin_amdgcn_update_dpp(ch, int(h[g]), kDppWaveShr1, 0xF, 0xF, false));
-            const uint32_t sl = uint32_t(__builtin_amdgcn_update_dpp(cl, int(l[g]), kDppWaveShr1, 0xF, 0xF, false));
-            const int idx = g * kWave + lane;
-            h[g] = idx > pos ? sh : (idx == pos ? kh : h[g]);
-            l[g] = idx > pos ? sl : (idx == pos ? kl : l[g]);
-            ch = lh;
-            cl = ll;
-        }
-    }
-};
-
-template <int G>
-struct PopState {
-    SortedFrontier<G> F;     // every offered key but `pending`
-    uint64_t pending;        // one more offered key (0: none)
-    LaneArray<G> nrho;       // float bits of each popped node's rho
-    LaneArray<G> ncur;       // rank of the child on offer (| kSlowNode)
-    LaneArray<G> qt, tt;     // candidate tables: entry pos * k + j
-    uint32_t qf, tf, ql, sf; // lane = position: q / token of rank 0, q of
-                             // rank k-1, rank order is safe at this position
-    const float *qtab;       // LDS copies of the tables (exact path)
-    const int32_t *ttab;
-    uint32_t *popm;          // LDS: popped-rank mask of exact-path nodes
-    int k;
-
-    // exact path: best child of node n (rho rn, depth dn + 1 children at
-    // position dn) among ranks not in `popped`; returns key, sets rank
-    __device__ __forceinline__ uint64_t exact_child(int n, float rn, int dn, uint32_t popped,
-                                                    int &rank) {
-        const int lane = lane_id();
-        const bool in = lane < k && !((popped >> lane) & 1u);
-        uint64_t key = 0;
-        if (in) key = tree_key(__fmul_rn(rn, qtab[dn * k + lane]), dn + 1, ttab[dn * k + lane], n);
-        const uint64_t best = wave_max_u64(key);
-        rank = best ? __ffsll((unsigned long long)__ballot(in && key == best)) - 1 : 0;
-        return best;
-    }
-
-    // node n (rho rn, depth dn < b) joins the tree: key of its first child
-    __device__ __forceinline__ uint64_t first_child(int n, float rn, int dn) {
-        const float q0 = __uint_as_float(uint32_t(__builtin_amdgcn_readlane(int(qf), dn)));
-        const float qk = __uint_as_float(uint32_t(__builtin_amdgcn_readlane(int(ql), dn)));
-        const uint32_t safe = uint32_t(__builtin_amdgcn_readlane(int(sf), dn));
-        uint64_t key;
-        uint32_t cur;
-        if (safe && __fmul_rn(rn, qk) >= 0x1p-125f) {
-            key = tree_key(__fmul_rn(rn, q0), dn + 1, __builtin_amdgcn_readlane(int(tf), dn), n);
-            cur = 0;
-        } else {
-            int rank;
-            key = exact_child(n, rn, dn, 0u, rank);
-            if (lane_id() == 0) popm[n] = 0u;
-            cur = uint32_t(rank) | kSlowNode;
-        }
-        nrho.set(n, __float_as_uint(rn));
-        ncur.set(n, cur);
-        return key;
-    }
-
-    // the child on offer at node p (at depth d) was popped: key of the next
-    __device__ __forceinline__ uint64_t next_child(int p, int d) {
-        const uint32_t cur = ncur.get(p);
-        const float rp = __uint_as_float(nrho.get(p));
-        uint64_t key = 0;
-        if (!(cur & kSlowNode)) {
-            const int c = int(cur) + 1;
-            if (c < k) {
-                const int e = (d - 1) * k + c;
-                key = tree_key(__fmul_rn(rp, __uint_as_float(qt.get(e))), d, int(tt.get(e)), p);
-            }
-            ncur.set(p, uint32_t(c));
-        } else {
-            const uint32_t popped = popm[p] | (1u << (cur & 255u));
-            int rank;
-            key = exact_child(p, rp, d - 1, popped, rank);
-            if (lane_id() == 0) popm[p] = popped;
-            ncur.set(p, uint32_t(rank) | kSlowNode);
-        }
-        return key;
-    }
-
-    // take the best offered key (0 when none is left)
-    __device__ __forceinline__ uint64_t pop() {
-        const uint64_t fr = F.front();
-        if (pending > fr) {
-            const uint64_t t = pending;
-            pending = 0;
-            return t;
-        }
-        if (fr) F.pop_front();
-        return fr;
-    }
-
-    // new offers: the best of (pending, a, c) stays pending, the rest go to
-    // the sorted array
-    __device__ __forceinline__ void offer(uint64_t a, uint64_t c) {
-        uint64_t x = pending, y = a, z = c;
-        if (y > x) { const uint64_t t = x; x = y; y = t; }
-        if (z > x) { const uint64_t t = x; x = z; z = t; }
-        pending = x;
-        if (y) F.insert(y);
-        if (z) F.insert(z);
-    }
-};
-
 template <int G>
 __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const TreeLayout L = tree_layout(P.b, P.k, P.nmax);
-    float *qtab = reinterpret_cast<float *>(smem + L.qtab);
-    int32_t *ttab = reinterpret_cast<int32_t *>(smem + L.ttab);
-    int32_t *par = reinterpret_cast<int32_t *>(smem + L.par);
-    int32_t *dep = reinterpret_cast<int32_t *>(smem + L.dep);
-    int32_t *tok = reinterpret_cast<int32_t *>(smem + L.tok);
-    float *rho = reinterpret_cast<float *>(smem + L.rho);
-    uint32_t *popm = reinterpret_cast<uint32_t *>(smem + L.popm);
-    double *ahat = reinterpret_cast<double *>(smem + L.ahat);
-    double *cost = reinterpret_cast<double *>(smem + L.cost);
+    const TreeLayout TL = tree_layout(P.b, P.k, P.nmax);
+    RoundsLds S;
+    S.qtab = reinterpret_cast<float *>(smem + TL.qtab);
+    S.ttab = reinterpret_cast<int32_t *>(smem + TL.ttab);
+    S.col = reinterpret_cast<uint64_t *>(smem + TL.col);
+    S.par = reinterpret_cast<int32_t *>(smem + TL.par);
+    S.dep = reinterpret_cast<int32_t *>(smem + TL.dep);
+    S.tok = reinterpret_cast<int32_t *>(smem + TL.tok);
+    S.rho = reinterpret_cast<float *>(smem + TL.rho);
+    S.ahat = reinterpret_cast<double *>(smem + TL.ahat);
+    S.cost = reinterpret_cast<double *>(smem + TL.cost);
+    S.map = reinterpret_cast<int32_t *>(smem + TL.map);
+    S.base = reinterpret_cast<int32_t *>(smem + TL.base);
     __shared__ int s_bad, s_nstar, s_status;
-    const int b = P.b, k = P.k, bk = b * k;
+    const int b = P.b, k = P.k, bk = b * k, nmax = P.nmax;
 
     const int64_t tk0 = int64_t(q) * bk;
     for (int e = tid; e < bk; e += kThreads) {
-        qtab[e] = ld_agent(P.topk_q + tk0 + e);
-        ttab[e] = ld_agent(P.topk_ids + tk0 + e);
+        S.qtab[e] = ld_agent(P.topk_q + tk0 + e);
+        S.ttab[e] = ld_agent(P.topk_ids + tk0 + e);
     }
     const bool online = P.cost != nullptr;
     if (online)
-        for (int e = tid; e <= P.nmax; e += kThreads)
-            cost[e] = P.cost[int64_t(q) * P.cost_qstride + e];
+        for (int e = tid; e <= nmax; e += kThreads)
+            S.cost[e] = P.cost[int64_t(q) * P.cost_qstride + e];
     if (tid == 0) s_bad = 0;
     __syncthreads();
     if (tid < b && ld_agent(P.row_status + int64_t(q) * b + tid) != BASTION_Q_OK)
@@ -626,103 +448,93 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
     const bool bad = s_bad != 0;
 
     if (!bad && wv == 0) {
-        PopState<G> S;
-        S.qtab = qtab;
-        S.ttab = ttab;
-        S.popm = popm;
-        S.k = k;
+        const uint64_t lt = lanemask_lt();
+        TopList<G> R;
+        const int cnt = rounds_build<G>(R, S, b, k, nmax);
+        // rank of every node among the nodes of its depth -> pop index
+        int basev = 0;
+        for (int d = 1; d <= b; ++d) {
+            if (lane == 0) S.base[d] = basev;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const uint64_t key = (uint64_t(R.h[g]) << 32) | R.l[g];
+                const bool v = key != 0 && tree_key_depth(key) == d;
+                const uint64_t msk = __ballot(v);
+                if (v) S.map[basev + popc64(msk & lt)] = g * kWave + lane + 1;
+                basev += popc64(msk);
+            }
+        }
+        wave_sync();
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const int e = lane + kWave * g;
-            S.qt.r[g] = e < bk ? __float_as_uint(qtab[e]) : 0u;
-            S.tt.r[g] = e < bk ? uint32_t(ttab[e]) : 0u;
-        }
-        S.qf = S.tf = S.ql = S.sf = 0;
-        if (lane < b) {
-            const int o = lane * k;
-            S.qf = __float_as_uint(qtab[o]);
-            S.tf = uint32_t(ttab[o]);
-            S.ql = __float_as_uint(qtab[o + k - 1]);
-            // rank order is the pop order at this position for every parent
-            // whose products stay normal, unless two neighbours are within
-            // 2^-22 of each other with the larger token first
-            uint32_t safe = 1;
-            for (int j = 0; j + 1 < k; ++j) {
-                const double a = qtab[o + j], c = qtab[o + j + 1];
-                if (ttab[o + j] > ttab[o + j + 1] && a < c * (1.0 + 0x1p-22)) safe = 0;
+            const int e = g * kWave + lane;
+            if (e < cnt) {
+                const uint64_t key = (uint64_t(R.h[g]) << 32) | R.l[g];
+                const int d = tree_key_depth(key);
+                const int pf = tree_key_parent(key);
+                int mi = S.base[d - 1] + pf;
+                mi = mi < nmax ? mi : nmax;   // a valid tree never needs the clamp
+                S.par[e + 1] = d == 1 ? 0 : S.map[mi];
+                S.dep[e + 1] = d;
+                S.tok[e + 1] = tree_key_token(key);
+                S.rho[e + 1] = tree_key_rho(key);
             }
-            S.sf = safe;
         }
-        S.F.clear();
-        S.pending = 0;
-        S.nrho.fill(0);
-        S.ncur.fill(0);
         if (lane == 0) {
-            par[0] = -1;
-            dep[0] = 0;
-            tok[0] = -1;
-            rho[0] = 1.0f;
-            ahat[0] = 1.0;
+            S.par[0] = -1;
+            S.dep[0] = 0;
+            S.tok[0] = -1;
+            S.rho[0] = 1.0f;
+            S.ahat[0] = 1.0;
         }
-        S.offer(S.first_child(0, 1.0f, 0), 0);
-        int count = 0, nstar = -1, status = BASTION_Q_OK;
+        // A_hat: float64 running sum in pop order (the order best-first adds)
         double ah = 1.0;
-        double s_prev = online ? (1.0 * P.l_ar) / cost[0] : 0.0;
-        while (true) {
-            const uint64_t top = S.pop();
-            if (top == 0) {
-                nstar = count;
-                status = count < P.nmax ? BASTION_Q_EXHAUSTED : BASTION_Q_OK;
-                break;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int n_here = cnt - g * kWave;
+            const int lim = n_here < kWave ? n_here : kWave;
+            for (int l = 0; l < lim; ++l) {
+                const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(R.h[g]), l));
+                ah += double(__uint_as_float((hi >> 2) - 1u));
+                if (lane == 0) S.ahat[g * kWave + l + 1] = ah;
             }
-            const int p = tree_key_parent(top);
-            const int d = tree_key_depth(top);
-            const int tkn = tree_key_token(top);
-            const float r = tree_key_rho(top);
-            const int n = count + 1;
-            const double ah_n = ah + double(r);
-            if (online) {
-                const double s_n = (ah_n * P.l_ar) / cost[n];
-                if (n - 1 >= P.nmin && s_n < s_prev) {
-                    nstar = n - 1;
+        }
+        wave_sync();
+        int nstar = cnt;
+        if (online) {
+            // the first n >= nmin with S(n+1) < S(n)
+            for (int c0 = 0; c0 < cnt; c0 += kWave) {
+                const int n = c0 + lane;
+                bool dec = false;
+                if (n < cnt && n >= P.nmin) {
+                    const double s0 = (S.ahat[n] * P.l_ar) / S.cost[n];
+                    const double s1 = (S.ahat[n + 1] * P.l_ar) / S.cost[n + 1];
+                    dec = s1 < s0;
+                }
+                const uint64_t msk = __ballot(dec);
+                if (msk) {
+                    nstar = c0 + __ffsll((unsigned long long)msk) - 1;
                     break;
                 }
-                s_prev = s_n;
             }
-            count = n;
-            ah = ah_n;
-            if (lane == 0) {
-                par[n] = p;
-                dep[n] = d;
-                tok[n] = tkn;
-                rho[n] = r;
-                ahat[n] = ah_n;
-            }
-            if (count == P.nmax) {
-                nstar = count;
-                break;
-            }
-            const uint64_t sib = S.next_child(p, d);
-            const uint64_t kid = d < b ? S.first_child(n, r, d) : 0;
-            S.offer(sib, kid);
         }
         if (lane == 0) {
             s_nstar = nstar;
-            s_status = status;
+            s_status = (nstar == cnt && cnt < nmax) ? BASTION_Q_EXHAUSTED : BASTION_Q_OK;
         }
     }
     __syncthreads();
     const int nstar = bad ? 0 : s_nstar;
     const int status = bad ? BASTION_Q_BAD_LOGITS : s_status;
-    const int W1 = P.nmax + 1;
+    const int W1 = nmax + 1;
     const int64_t o = int64_t(q) * W1;
     for (int i = tid; i < W1; i += kThreads) {
         const bool v = i <= nstar && !bad;
-        P.parent[o + i] = v ? (i == 0 ? -1 : par[i]) : -1;
-        P.depth[o + i] = v ? (i == 0 ? 0 : dep[i]) : -1;
-        P.token[o + i] = v ? (i == 0 ? -1 : tok[i]) : -1;
-        P.rho[o + i] = v ? (i == 0 ? 1.0f : rho[i]) : 0.0f;
-        P.ahat[o + i] = v ? (i == 0 ? 1.0 : ahat[i]) : 0.0;
+        P.parent[o + i] = v ? (i == 0 ? -1 : S.par[i]) : -1;
+        P.depth[o + i] = v ? (i == 0 ? 0 : S.dep[i]) : -1;
+        P.token[o + i] = v ? (i == 0 ? -1 : S.tok[i]) : -1;
+        P.rho[o + i] = v ? (i == 0 ? 1.0f : S.rho[i]) : 0.0f;
+        P.ahat[o + i] = v ? (i == 0 ? 1.0 : S.ahat[i]) : 0.0;
     }
     if (bad && tid == 0) {
         P.parent[o] = -1;
@@ -746,7 +558,7 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
                 int j = i;
                 if (j / 32 == w) bits |= 1u << (j & 31);
                 while (j > 0 && steps < b) {
-                    j = par[j];
+                    j = S.par[j];
                     ++steps;
                     if (j / 32 == w) bits |= 1u << (j & 31);
                 }
@@ -869,13 +681,14 @@ static hipError_t launch_one(const BuildParams &P, int smem, hipStream_t s) {
 
 template <typename T, int U>
 static hipError_t launch_r(const BuildParams &P, int smem, hipStream_t s) {
-    // lane arrays must hold nmax + 1 slots and b * k table entries
-    const int slots = (P.nmax + 1) > (P.b * P.k) ? (P.nmax + 1) : (P.b * P.k);
-    if (slots <= 64) return launch_one<T, U, 1>(P, smem, s);
-    if (slots <= 128) return launch_one<T, U, 2>(P, smem, s);
-    if (slots <= 256) return launch_one<T, U, 4>(P, smem, s);
-    if (slots <= 512) return launch_one<T, U, 8>(P, smem, s);
-    return launch_one<T, U, 16>(P, smem, s);
+    // the running top-N list holds nmax keys in tree_regs(nmax) registers
+    switch (tree_regs(P.nmax)) {
+        case 1: return launch_one<T, U, 1>(P, smem, s);
+        case 2: return launch_one<T, U, 2>(P, smem, s);
+        case 4: return launch_one<T, U, 4>(P, smem, s);
+        case 8: return launch_one<T, U, 8>(P, smem, s);
+        default: return launch_one<T, U, 16>(P, smem, s);
+    }
 }
 
 }  // namespace bastion
