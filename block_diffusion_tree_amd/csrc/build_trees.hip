@@ -15,6 +15,7 @@
 #include "device_common.hpp"
 #include "build_params.hpp"
 #include "tree_rounds.hpp"
+#include "tree_pool.hpp"
 
 namespace bastion {
 
@@ -268,7 +269,20 @@ __device__ SegmentResult stream_segment(const BuildParams &P, const char *row, i
     };
     if (ntiles > 0) fill(A, 0);
     int t = 0;
+    // The instruction arbiter favours older waves, so the blocks sharing a
+    // CU would otherwise finish one after another and leave the CU with a
+    // single streaming block at the end.  A wave's priority falls as its
+    // segment progresses, which keeps the co-resident blocks level.
+    int tier = -1;
     for (; t + 1 < ntiles; t += 2) {
+        const int nt = (4 * t) / ntiles;
+        if (nt != tier) {
+            tier = nt;
+            if (nt == 0) __builtin_amdgcn_s_setprio(3);
+            else if (nt == 1) __builtin_amdgcn_s_setprio(2);
+            else if (nt == 2) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        }
         fill(Bv, t + 1);
         st.tile(A, vlo + t * span, all, sm);
         if (t + 2 < ntiles) fill(A, t + 2);
@@ -384,21 +398,26 @@ __device__ bool arrive_last(uint32_t *ticket, uint32_t total) {
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
 
+// LDS row stride of the q / token tables: k padded to a multiple of 8
+__host__ __device__ inline int qrow_stride(int k) { return (k + 7) & ~7; }
+
 __host__ __device__ inline int tree_regs(int nmax) {
     const int need = (nmax + kWave - 1) / kWave;
     return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
 }
 
 struct TreeLayout {
-    int qtab, ttab, col, par, dep, tok, rho, ahat, cost, map, base, total;
+    int qtab, ttab, col, par, dep, tok, rho, ahat, cost, map, base;
+    int pkey, ppar, prho, plrank, ppop, hist, plvl, q0col, total;
 };
 
 __host__ __device__ inline TreeLayout tree_layout(int b, int k, int nmax) {
     TreeLayout L;
     const int nn = nmax + 2;
+    const int cap = pool_cap(tree_regs(nmax));
     int o = 0;
-    L.qtab = o; o = align16(o + 4 * b * k);
-    L.ttab = o; o = align16(o + 4 * b * k);
+    L.qtab = o; o = align16(o + 4 * b * qrow_stride(k));
+    L.ttab = o; o = align16(o + 4 * b * qrow_stride(k));
     L.col = o;  o = align16(o + 8 * kWave * tree_regs(nmax));
     L.par = o;  o = align16(o + 4 * nn);
     L.dep = o;  o = align16(o + 4 * nn);
@@ -408,8 +427,60 @@ __host__ __device__ inline TreeLayout tree_layout(int b, int k, int nmax) {
     L.cost = o; o = align16(o + 8 * nn);
     L.map = o;  o = align16(o + 4 * nn);
     L.base = o; o = align16(o + 4 * 40);
+    L.pkey = o; o = align16(o + 8 * (cap + kPoolPad));
+    L.ppar = o; o = align16(o + 4 * cap);
+    L.prho = o; o = align16(o + 4 * cap);
+    L.ppop = o; o = align16(o + 4 * cap);
+    L.plrank = o; o = align16(o + 4 * cap);
+    L.hist = o; o = align16(o + (cap > 0 ? 4 * kHistBins : 0));
+    L.plvl = o; o = align16(o + (cap > 0 ? 4 * kLvlFloats : 0));
+    L.q0col = o; o = align16(o + 4 * kMaxB);
     L.total = o;
     return L;
+}
+
+__device__ __forceinline__ uint32_t *TL_hist(char *smem, const TreeLayout &TL) {
+    return reinterpret_cast<uint32_t *>(smem + TL.hist);
+}
+
+// The exact round-by-round build of tree_rounds.hpp plus parent resolution:
+// pop-order records 1..cnt into S.par/dep/tok/rho; returns cnt (one wave).
+template <int G>
+__device__ int exact_build(const RoundsLds &S, int b, int k, int nmax) {
+    const int lane = lane_id();
+    const uint64_t lt = lanemask_lt();
+    TopList<G> R;
+    const int cnt = rounds_build<G>(R, S, b, k, nmax);
+    // rank of every node among the nodes of its depth -> pop index
+    int basev = 0;
+    for (int d = 1; d <= b; ++d) {
+        if (lane == 0) S.base[d] = basev;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const uint64_t key = (uint64_t(R.h[g]) << 32) | R.l[g];
+            const bool v = key != 0 && tree_key_depth(key) == d;
+            const uint64_t msk = __ballot(v);
+            if (v) S.map[basev + popc64(msk & lt)] = g * kWave + lane + 1;
+            basev += popc64(msk);
+        }
+    }
+    wave_sync();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int e = g * kWave + lane;
+        if (e < cnt) {
+            const uint64_t key = (uint64_t(R.h[g]) << 32) | R.l[g];
+            const int d = tree_key_depth(key);
+            const int pf = tree_key_parent(key);
+            int mi = S.base[d - 1] + pf;
+            mi = mi < nmax ? mi : nmax;   // a valid tree never needs the clamp
+            S.par[e + 1] = d == 1 ? 0 : S.map[mi];
+            S.dep[e + 1] = d;
+            S.tok[e + 1] = tree_key_token(key);
+            S.rho[e + 1] = tree_key_rho(key);
+        }
+    }
+    return cnt;
 }
 
 template <int G>
@@ -432,10 +503,17 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
     const int b = P.b, k = P.k, bk = b * k, nmax = P.nmax;
 
     const int64_t tk0 = int64_t(q) * bk;
-    for (int e = tid; e < bk; e += kThreads) {
-        S.qtab[e] = ld_agent(P.topk_q + tk0 + e);
-        S.ttab[e] = ld_agent(P.topk_ids + tk0 + e);
+    const int kp = qrow_stride(k);
+    S.kp = kp;
+    float *q0col = reinterpret_cast<float *>(smem + TL.q0col);
+    for (int e = tid; e < b * kp; e += kThreads) {
+        const int d = e / kp, j = e - d * kp;
+        const float qv = j < k ? ld_agent(P.topk_q + tk0 + d * k + j) : 0.0f;
+        S.qtab[e] = qv;
+        S.ttab[e] = j < k ? ld_agent(P.topk_ids + tk0 + d * k + j) : 0;
+        if (j == 0) q0col[d] = qv;
     }
+    for (int d = b + tid; d < kMaxB; d += kThreads) q0col[d] = 0.0f;
     const bool online = P.cost != nullptr;
     if (online)
         for (int e = tid; e <= nmax; e += kThreads)
@@ -447,39 +525,33 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
     __syncthreads();
     const bool bad = s_bad != 0;
 
+    constexpr int kPoolCap = pool_cap(G);
+    __shared__ float s_bound;
+    __shared__ int s_pool;
+    int cnt = -1;
+    if (kPoolCap > 0 && !bad) {
+        PoolLds PL;
+        PL.key = reinterpret_cast<uint64_t *>(smem + TL.pkey);
+        PL.par = reinterpret_cast<int32_t *>(smem + TL.ppar);
+        PL.rho = reinterpret_cast<float *>(smem + TL.prho);
+        PL.pop = reinterpret_cast<int32_t *>(smem + TL.ppop);
+        PL.lrank = reinterpret_cast<int32_t *>(smem + TL.plrank);
+        PL.hist = reinterpret_cast<uint32_t *>(smem + TL.hist);
+        const float bound = family_bound<kThreads>(S.qtab, q0col, b, k, kp, nmax, PL.hist,
+                                                   reinterpret_cast<float *>(smem + TL.plvl),
+                                                   &s_bound);
+        if (wv == 0) {
+            const int n = pool_enumerate(PL, S.qtab, S.ttab, b, k, kp, bound, kPoolCap);
+            if (lane == 0) s_pool = n;
+        }
+        __syncthreads();
+        const int n = s_pool;
+        if (n >= 1) cnt = pool_rank<kThreads>(PL, n, nmax, S.par, S.dep, S.tok, S.rho);
+        __syncthreads();
+    }
+
     if (!bad && wv == 0) {
-        const uint64_t lt = lanemask_lt();
-        TopList<G> R;
-        const int cnt = rounds_build<G>(R, S, b, k, nmax);
-        // rank of every node among the nodes of its depth -> pop index
-        int basev = 0;
-        for (int d = 1; d <= b; ++d) {
-            if (lane == 0) S.base[d] = basev;
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const uint64_t key = (uint64_t(R.h[g]) << 32) | R.l[g];
-                const bool v = key != 0 && tree_key_depth(key) == d;
-                const uint64_t msk = __ballot(v);
-                if (v) S.map[basev + popc64(msk & lt)] = g * kWave + lane + 1;
-                basev += popc64(msk);
-            }
-        }
-        wave_sync();
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int e = g * kWave + lane;
-            if (e < cnt) {
-                const uint64_t key = (uint64_t(R.h[g]) << 32) | R.l[g];
-                const int d = tree_key_depth(key);
-                const int pf = tree_key_parent(key);
-                int mi = S.base[d - 1] + pf;
-                mi = mi < nmax ? mi : nmax;   // a valid tree never needs the clamp
-                S.par[e + 1] = d == 1 ? 0 : S.map[mi];
-                S.dep[e + 1] = d;
-                S.tok[e + 1] = tree_key_token(key);
-                S.rho[e + 1] = tree_key_rho(key);
-            }
-        }
+        if (cnt < 0) cnt = exact_build<G>(S, b, k, nmax);
         if (lane == 0) {
             S.par[0] = -1;
             S.dep[0] = 0;
@@ -487,16 +559,24 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
             S.rho[0] = 1.0f;
             S.ahat[0] = 1.0;
         }
+        wave_sync();
         // A_hat: float64 running sum in pop order (the order best-first adds)
-        double ah = 1.0;
+        if (lane == 0) {
+            double ah = 1.0;
+            int n = 1;
+            for (; n + 8 <= cnt + 1; n += 8) {
+                float r[8];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int n_here = cnt - g * kWave;
-            const int lim = n_here < kWave ? n_here : kWave;
-            for (int l = 0; l < lim; ++l) {
-                const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(R.h[g]), l));
-                ah += double(__uint_as_float((hi >> 2) - 1u));
-                if (lane == 0) S.ahat[g * kWave + l + 1] = ah;
+                for (int i = 0; i < 8; ++i) r[i] = S.rho[n + i];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    ah += double(r[i]);
+                    S.ahat[n + i] = ah;
+                }
+            }
+            for (; n <= cnt; ++n) {
+                ah += double(S.rho[n]);
+                S.ahat[n] = ah;
             }
         }
         wave_sync();

@@ -189,8 +189,9 @@ struct TopList {
 };
 
 struct RoundsLds {
-    float *qtab;       // [b * k] candidate q of each position, rank order
-    int32_t *ttab;     // [b * k] candidate tokens
+    float *qtab;       // [b * kp] candidate q of each position, rank order
+    int32_t *ttab;     // [b * kp] candidate tokens (rows padded to kp)
+    int kp;            // row stride: k rounded up to a multiple of 8
     uint64_t *col;     // [64 * G] compaction buffer for one column
     int32_t *par, *dep, *tok;   // [nmax + 2] node records (pop order)
     float *rho;
@@ -238,8 +239,8 @@ __device__ int rounds_build(TopList<G> &R, const RoundsLds &S, int b, int k, int
         if (m == 0) break;
         uint64_t tau = cnt == nmax ? R.at(nmax - 1) : 0;
         for (int j = 0; j < k; ++j) {
-            const float qj = S.qtab[(d - 1) * k + j];
-            const int tj = S.ttab[(d - 1) * k + j];
+            const float qj = S.qtab[(d - 1) * S.kp + j];
+            const int tj = S.ttab[(d - 1) * S.kp + j];
             uint64_t ck[G];
             int L = 0;
             int off[G];

@@ -135,6 +135,24 @@ def test_integer_logits_many_ties():
     gc.run_and_check(x, 8, 60)
 
 
+def test_flat_rows_overflow_the_pool():
+    """Equal logits: every node of a depth has the same rho, so a budget of
+    100 with k = 8 reaches into the 512 depth-3 nodes and the candidate pool
+    of the fast path (256 slots at this budget) overflows; the exact
+    round-by-round build must produce the same tree."""
+    x = torch.zeros((2, 4, 3001), dtype=torch.bfloat16, device="cuda")
+    g, _ = gc.run_and_check(x, 8, 100)
+    assert (gc.np_(g["depth"])[:, 1:9] == 1).all()
+
+
+def test_near_flat_rows_fill_the_pool():
+    """Small integer logits over few tokens: wide, tie-heavy levels that fit
+    the pool (budget 120, 256 slots)."""
+    torch.manual_seed(5)
+    x = torch.randint(0, 2, (3, 5, 64)).float().to("cuda")
+    gc.run_and_check(x, 6, 120)
+
+
 def test_row_stride_padding_and_pos_base():
     wl = synth.scaled(synth.WORKLOADS["main"], B=2, b=4, V=1000, nmax=20)
     base = synth.make_logits(wl)
