@@ -427,11 +427,11 @@ __host__ __device__ inline TreeLayout tree_layout(int b, int k, int nmax) {
     L.cost = o; o = align16(o + 8 * nn);
     L.map = o;  o = align16(o + 4 * nn);
     L.base = o; o = align16(o + 4 * 40);
-    L.pkey = o; o = align16(o + 8 * (cap + kPoolPad));
+    L.pkey = o; o = align16(o + 8 * cap);
     L.ppar = o; o = align16(o + 4 * cap);
     L.prho = o; o = align16(o + 4 * cap);
-    L.ppop = o; o = align16(o + 4 * cap);
     L.plrank = o; o = align16(o + 4 * cap);
+    L.ppop = o; o = align16(o + 4 * cap);
     L.hist = o; o = align16(o + (cap > 0 ? 4 * kHistBins : 0));
     L.plvl = o; o = align16(o + (cap > 0 ? 4 * kLvlFloats : 0));
     L.q0col = o; o = align16(o + 4 * kMaxB);
@@ -534,8 +534,8 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
         PL.key = reinterpret_cast<uint64_t *>(smem + TL.pkey);
         PL.par = reinterpret_cast<int32_t *>(smem + TL.ppar);
         PL.rho = reinterpret_cast<float *>(smem + TL.prho);
-        PL.pop = reinterpret_cast<int32_t *>(smem + TL.ppop);
         PL.lrank = reinterpret_cast<int32_t *>(smem + TL.plrank);
+        PL.pop = reinterpret_cast<int32_t *>(smem + TL.ppop);
         PL.hist = reinterpret_cast<uint32_t *>(smem + TL.hist);
         const float bound = family_bound<kThreads>(S.qtab, q0col, b, k, kp, nmax, PL.hist,
                                                    reinterpret_cast<float *>(smem + TL.plvl),

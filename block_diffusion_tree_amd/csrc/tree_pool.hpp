@@ -14,16 +14,19 @@
 //   2. one wave enumerates, level by level, every node with rho >= t.  A
 //      parent's children come in rank order with non-increasing rho (q is
 //      sorted and float products are monotone), so each parent contributes
-//      a prefix of its ranks.  Right after a level is generated its nodes
-//      are ranked among themselves by (rho, token, parent's rank in its own
-//      level); that is best-first's order inside one depth, since the pop
-//      order of same-depth parents is their in-level order.  The key of a
-//      node carries its parent's in-level rank, so keys are unique and
-//      compare exactly as best-first does.  The caller falls back to the
-//      exact round-by-round build if the pool outgrows its capacity.
-//   3. every pool entry counts the keys larger than its own (all 256
-//      threads, the comparisons split over the waves); the count is its pop
-//      index minus one, and the first min(pool, N) entries are the tree.
+//      a prefix of its ranks.  Such pools are a few parallel chains that
+//      branch at uncertain positions: each lane carries one chain in
+//      registers.  A node's key holds its parent's rank inside the parent's
+//      level, which is best-first's order for children of different parents
+//      that agree on (rho, depth, token); keys are then unique and compare
+//      exactly as best-first pops.  On a level where no chain branches, each
+//      child keeps its parent's in-level rank (same token, monotone rho, and
+//      the chains that stop are the last ones), so only branching levels
+//      rank their nodes, through LDS.  Levels wider than a wave are expanded
+//      from LDS.  The caller falls back to the exact round-by-round build if
+//      the pool outgrows its capacity.
+//   3. the block counts, for every pool node, the larger keys; the count is
+//      its pop index minus one, and the first min(pool, N) are the tree.
 #pragma once
 
 #include "device_common.hpp"
@@ -41,13 +44,15 @@ __host__ __device__ constexpr int pool_cap(int G) { return G <= 8 ? 128 * G : 0;
 constexpr int kLvlFloats = kFamilyLevels;   // family scratch
 
 typedef uint32_t pool_u32x4 __attribute__((ext_vector_type(4)));
+typedef float pool_f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t pool_i32x4 __attribute__((ext_vector_type(4)));
 
 struct PoolLds {
-    uint64_t *key;     // [cap] by slot
+    uint64_t *key;     // [cap] tree_key, parent field = parent's in-level rank
     int32_t *par;      // [cap] parent slot, -1 for the root
     float *rho;        // [cap]
     int32_t *lrank;    // [cap] rank inside its level
-    int32_t *pop;      // [cap] slot -> pop index (minus one while counting)
+    int32_t *pop;      // [cap] pop index
     uint32_t *hist;    // [kHistBins]
 };
 
@@ -183,94 +188,179 @@ __device__ __forceinline__ int count_greater(const uint64_t *keys, int f0, int f
     return r;
 }
 
-// Step 2, by one wave: every node with rho >= t, parents before children.
-// Lane l handles rank l % kk of parent l / kk of a chunk (kk: k rounded up
-// to a power of two).  L.key has kPoolPad spare slots past cap, so a level
-// can be ranked with unconditional loads of zero-padded keys.  Returns the
-// node count, or -1 past cap.
-constexpr int kPoolPad = 16;
+// in-level ranks of slots [n0, n) (one wave)
+__device__ __forceinline__ void rank_level(const PoolLds &L, int n0, int n) {
+    const int lane = lane_id();
+    for (int s0 = n0; s0 < n; s0 += kWave) {
+        const int s = s0 + lane;
+        const uint64_t x = s < n ? L.key[s] : ~uint64_t(0);
+        const int r = count_greater(L.key, n0, n, x);
+        if (s < n) L.lrank[s] = r;
+    }
+}
 
+// Step 2, by one wave: every node with rho >= t, parents before children.
+// Returns the node count, or -1 past cap.
 __device__ int pool_enumerate(const PoolLds &L, const float *qtab, const int32_t *ttab, int b,
                               int k, int kp, float t, int cap) {
     const int lane = lane_id();
     const uint64_t lt = lanemask_lt();
-    int sh = 0;
-    while ((1 << sh) < k) ++sh;
-    const int pl = lane >> sh, j = lane & ((1 << sh) - 1), ppc = kWave >> sh;
-    const int jc = j < k ? j : k - 1;
-    // counts are wave-uniform; readfirstlane keeps them in scalar registers
-    int lo = 0, hi = 0, n = 0;
-    bool over = false;
-    float qj = qtab[jc];
-    int tj = ttab[jc];
-    for (int d = 1; d <= b; ++d) {
-        const int np = __builtin_amdgcn_readfirstlane(d == 1 ? 1 : hi - lo);
-        if (np == 0) break;
-        // the next level's q and token, loaded one level ahead
-        const int dn = d < b ? d : 0;
-        const float qn = qtab[dn * kp + jc];
-        const int tn = ttab[dn * kp + jc];
-        const int n0 = n;
-        if (lane < kPoolPad) L.key[n0 + lane] = 0;   // padding for the ranking below
-        for (int p0 = 0; p0 < np; p0 += ppc) {
-            const int p = p0 + pl;
-            const bool valid = p < np && j < k;
-            const int pc = lo + (p < np ? p : np - 1);
-            const float rp = d == 1 ? 1.0f : L.rho[pc];
-            const int pr = d == 1 ? 0 : L.lrank[pc];
-            const float v = __fmul_rn(rp, qj);
-            const bool ok = valid && v >= t;
-            const uint64_t m = __ballot(ok);
+    // lane l < 32 holds q of rank 0 at depth l+1, lane 32 + l that of rank 1;
+    // tok0: token of rank 0 at depth l+1
+    const int dl = lane & 31;
+    const int dr = dl < b ? dl : 0;
+    const float colq = qtab[dr * kp + (lane >= 32 && k > 1 ? 1 : 0)];
+    const int tok0 = ttab[dr * kp];
+    // level 1: the root's children are the ranks with q >= t, a prefix, and
+    // their in-level order is the rank order
+    const float q1v = lane < k ? qtab[lane] : 0.0f;
+    const bool ok1 = lane < k && q1v >= t;
+    int n = __builtin_amdgcn_readfirstlane(popc64(__ballot(ok1)));
+    if (n > cap) return -1;
+    if (ok1) {
+        L.key[lane] = tree_key(q1v, 1, ttab[lane], 0);
+        L.par[lane] = -1;
+        L.rho[lane] = q1v;
+        L.lrank[lane] = lane;
+    }
+    bool alive = ok1;
+    float rho = q1v;
+    int slot = lane, lr = lane;
+    int lo = 0, hi = n, d = 2;
+    bool wide = false, over = false;
+    // chains in lanes
+    for (; d <= b && hi > lo; ++d) {
+        const float q0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(colq), d - 1));
+        const float q1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(colq), 32 + d - 1));
+        const float v0 = __fmul_rn(rho, q0);
+        const bool ok0 = alive && v0 >= t;
+        const bool br = alive && k > 1 && __fmul_rn(rho, q1) >= t;
+        if (__ballot(br) == 0) {
+            // no chain branches: each continues with its rank-0 child, which
+            // keeps the parent's in-level rank
+            const uint64_t m = __ballot(ok0);
             const int c = __builtin_amdgcn_readfirstlane(popc64(m));
             if (n + c > cap) {
                 over = true;
                 break;
             }
+            const int s = n + popc64(m & lt);
+            const int t0 = __builtin_amdgcn_readlane(tok0, d - 1);
+            if (ok0) {
+                L.key[s] = tree_key(v0, d, t0, lr);
+                L.par[s] = slot;
+                L.rho[s] = v0;
+                L.lrank[s] = lr;
+            }
+            alive = ok0;
+            rho = v0;
+            slot = s;
+            lo = n;
+            n = __builtin_amdgcn_readfirstlane(n + c);
+            hi = n;
+        } else {
+            // every child of the level, rank by rank; then rank the level
+            // and hand its nodes to the lanes
+            const int n0 = n;
+            for (int j0 = 0; j0 < k; j0 += 8) {
+                // eight ranks at a time, loaded together (zero padding past k)
+                const pool_f32x4 *q4 = reinterpret_cast<const pool_f32x4 *>(qtab + (d - 1) * kp + j0);
+                const pool_i32x4 *t4 = reinterpret_cast<const pool_i32x4 *>(ttab + (d - 1) * kp + j0);
+                const pool_f32x4 qa = q4[0], qb = q4[1];
+                const pool_i32x4 ta = t4[0], tb = t4[1];
+                const float qv[8] = {qa[0], qa[1], qa[2], qa[3], qb[0], qb[1], qb[2], qb[3]};
+                const int tv[8] = {ta[0], ta[1], ta[2], ta[3], tb[0], tb[1], tb[2], tb[3]};
+                float v[8];
+                uint64_t m[8];
+                int c[8], tot = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    v[i] = __fmul_rn(rho, qv[i]);
+                    m[i] = __ballot(alive && j0 + i < k && v[i] >= t);
+                    c[i] = popc64(m[i]);
+                    tot += c[i];
+                }
+                tot = __builtin_amdgcn_readfirstlane(tot);
+                if (n + tot > cap) {
+                    over = true;
+                    break;
+                }
+                int base = n;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    if ((m[i] >> lane) & 1u) {
+                        const int s = base + popc64(m[i] & lt);
+                        L.key[s] = tree_key(v[i], d, tv[i], lr);
+                        L.par[s] = slot;
+                        L.rho[s] = v[i];
+                    }
+                    base += c[i];
+                }
+                n = __builtin_amdgcn_readfirstlane(n + tot);
+                if (m[7] == 0) break;   // later ranks give no larger rho
+            }
+            if (over) break;
+            wave_sync();
+            rank_level(L, n0, n);
+            wave_sync();
+            lo = n0;
+            hi = n;
+            if (hi - lo > kWave) {
+                wide = true;
+                ++d;
+                break;
+            }
+            alive = lane < hi - lo;
+            slot = lo + (alive ? lane : 0);
+            rho = alive ? L.rho[slot] : 0.0f;
+            lr = alive ? L.lrank[slot] : 0;
+        }
+    }
+    if (over) return -1;
+    if (!wide) return n;
+    // levels wider than a wave: lane l handles rank l % kk of parent l / kk
+    // of a chunk (kk: k rounded up to a power of two)
+    int sh = 0;
+    while ((1 << sh) < k) ++sh;
+    const int pl = lane >> sh, j = lane & ((1 << sh) - 1), ppc = kWave >> sh;
+    const int jc = j < k ? j : k - 1;
+    for (; d <= b && hi > lo; ++d) {
+        const int np = hi - lo;
+        const float qj = qtab[(d - 1) * kp + jc];
+        const int tj = ttab[(d - 1) * kp + jc];
+        const int n0 = n;
+        for (int p0 = 0; p0 < np; p0 += ppc) {
+            const int p = p0 + pl;
+            const bool valid = p < np && j < k;
+            const int pc = lo + (p < np ? p : np - 1);
+            const float v = __fmul_rn(L.rho[pc], qj);
+            const int pr = L.lrank[pc];
+            const bool ok = valid && v >= t;
+            const uint64_t m = __ballot(ok);
+            const int c = __builtin_amdgcn_readfirstlane(popc64(m));
+            if (n + c > cap) return -1;
             if (ok) {
                 const int s = n + popc64(m & lt);
                 L.key[s] = tree_key(v, d, tj, pr);
-                L.par[s] = d == 1 ? -1 : lo + p;
+                L.par[s] = pc;
                 L.rho[s] = v;
             }
             n = __builtin_amdgcn_readfirstlane(n + c);
         }
-        if (over) break;
         wave_sync();
-        // rank the level's nodes among themselves (keys are unique)
-        const int m = n - n0;
-        if (m == 1) {
-            if (lane == 0) L.lrank[n0] = 0;
-        } else if (m <= kPoolPad) {
-            const uint64_t x = L.key[n0 + (lane < m ? lane : 0)];
-            uint64_t y[kPoolPad];
-#pragma unroll
-            for (int i = 0; i < kPoolPad; ++i) y[i] = L.key[n0 + i];
-            int r = 0;
-#pragma unroll
-            for (int i = 0; i < kPoolPad; ++i) r += y[i] > x ? 1 : 0;
-            if (lane < m) L.lrank[n0 + lane] = r;
-        } else {
-            for (int s0 = n0; s0 < n; s0 += kWave) {
-                const int s = s0 + lane;
-                const uint64_t x = s < n ? L.key[s] : ~uint64_t(0);
-                const int r = count_greater(L.key, n0, n, x);
-                if (s < n) L.lrank[s] = r;
-            }
-        }
+        rank_level(L, n0, n);
         wave_sync();
         lo = hi;
         hi = n;
-        qj = qn;
-        tj = tn;
     }
-    return over ? -1 : n;
+    return n;
 }
 
-// Step 3, by the whole block (n >= 1).  L.pop[s] receives the pop index of
-// slot s; the pop-order records 1..cnt (cnt =
-// min(n, nmax)) go to par/dep/tok/rho.  Elements are taken 64 per wave; when
-// there are fewer than four such groups the waves of a group split the
-// comparisons and add their counts.  Returns cnt.
+// Step 3, by the whole block (n >= 1): the pop index of every pool node
+// (L.pop) and the pop-order records 1..cnt (cnt = min(n, nmax)) in
+// par/dep/tok/rho.  Nodes are taken 64 per wave; with fewer such groups than
+// waves, the waves of a group split the comparisons and add their counts.
+// Returns cnt.
 template <int THREADS>
 __device__ __forceinline__ int pool_rank(const PoolLds &L, int n, int nmax, int32_t *par,
                                          int32_t *dep, int32_t *tok, float *rho) {
@@ -279,28 +369,25 @@ __device__ __forceinline__ int pool_rank(const PoolLds &L, int n, int nmax, int3
     const int groups = (n + kWave - 1) / kWave;
     const int split = groups >= W ? 1 : W / groups;   // waves per group
     const int chunk = (n + split - 1) / split;
-    if (split > 1) {
-        for (int e = tid; e < n; e += THREADS) L.pop[e] = 0;
-        __syncthreads();
-    }
+    for (int e = tid; e < n; e += THREADS) L.pop[e] = 1;
+    __syncthreads();
     for (int g0 = wv / split; g0 < groups; g0 += W / split) {
         const int e = g0 * kWave + lane;
         const int part = wv % split;
         const int f0 = part * chunk, f1 = f0 + chunk < n ? f0 + chunk : n;
         if (e < n) {
             const int r = count_greater(L.key, f0, f1, L.key[e]);
-            if (split == 1) L.pop[e] = r + 1;
-            else if (r) atomicAdd(L.pop + e, r);
+            if (r) atomicAdd(L.pop + e, r);
         }
     }
     __syncthreads();
     const int cnt = n < nmax ? n : nmax;
     for (int e = tid; e < n; e += THREADS) {
-        const int pe = L.pop[e] + (split == 1 ? 0 : 1);
+        const int pe = L.pop[e];
         if (pe <= cnt) {
             const int ps = L.par[e];
             const uint64_t x = L.key[e];
-            par[pe] = ps < 0 ? 0 : L.pop[ps] + (split == 1 ? 0 : 1);
+            par[pe] = ps < 0 ? 0 : L.pop[ps];
             dep[pe] = tree_key_depth(x);
             tok[pe] = tree_key_token(x);
             rho[pe] = tree_key_rho(x);
