@@ -560,8 +560,28 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
             S.ahat[0] = 1.0;
         }
         wave_sync();
-        // A_hat: float64 running sum in pop order (the order best-first adds)
-        if (lane == 0) {
+        // A_hat: float64 running sum in pop order (the order best-first adds).
+        // When the smallest rho is at least 2^(L-30), with 2^L > cnt + 1,
+        // every rho is a multiple of ulp(smallest) and every partial sum is
+        // below 2^L, so all sums are exact in float64 and a parallel scan
+        // gives the same bits as the running sum.
+        const uint32_t rb = cnt >= 1 ? __float_as_uint(S.rho[cnt]) : 0u;
+        const int Lb = 32 - __clz(cnt + 1);
+        const bool exact = cnt >= 1 && (rb >> 23) != 0u && int(rb >> 23) - 127 >= Lb - 30;
+        if (exact) {
+            double carry = 1.0;
+            for (int c0 = 0; c0 < cnt; c0 += kWave) {
+                const int n = c0 + 1 + lane;
+                double v = n <= cnt ? double(S.rho[n]) : 0.0;
+#pragma unroll
+                for (int sft = 1; sft < kWave; sft <<= 1) {
+                    const double o = __shfl_up(v, sft);
+                    v += lane >= sft ? o : 0.0;
+                }
+                if (n <= cnt) S.ahat[n] = carry + v;
+                carry += __shfl(v, kWave - 1);
+            }
+        } else if (lane == 0) {
             double ah = 1.0;
             int n = 1;
             for (; n + 8 <= cnt + 1; n += 8) {
@@ -628,6 +648,7 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
         P.qstatus[q] = status;
     }
     if (P.mask) {
+        // one thread per (node, mask word), each walking up from the node
         const int W = (W1 + 31) / 32;
         const int32_t pb = P.pos_base ? P.pos_base[q] : 0;
         for (int e = tid; e < W1 * W; e += kThreads) {
