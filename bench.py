@@ -5,7 +5,10 @@
 A step is one bastion_build_trees call (softmax + top-k over the vocabulary,
 best-first tree with A_hat, mask and position ids) over one batch of
 synthetic logits that is already resident in HBM.  Four distinct input
-batches rotate so that no step finds its logits in the 256 MB MALL.
+batches rotate so that no step finds its logits in the 256 MB MALL.  With
+--workload mixture a step is one bastion_mixture_score call (branch rows,
+chains and q_dep, candidate unions, mixture tree with mask) over two
+rotating 5 GB batches.
 
 Prints one JSON line.  `value` is trees per second over the timed steps.
 `roofline` is the fused kernel's algorithmic bytes per launch (every logit
@@ -26,6 +29,7 @@ WORKLOAD_TEXT = {
     "sweep": "B=256 x b=16 x V=128256 fp32 logits, k=4, online stop over N<=256",
     "latency": "B=1 x b=16 x V=151936 bf16 logits, k=16, online stop over N<=128",
     "tiny": "B=1 x b=4 x V=1024 fp32 logits, k=4, fixed N=32",
+    "mixture": "B=128 queries x K=8 branches x b=16 x V=151936 bf16 logits, k=8, mixture tree N=64",
 }
 HBM_PEAK_GBS = 8000.0
 N_BUFFERS = 4
@@ -86,6 +90,29 @@ def cpu_baseline(x_host, wl, n_queries, min_seconds=2.0, max_reps=10):
                        f"mask; median of {len(times)} passes, {dt:.3f} s per pass"), rows
 
 
+def cpu_baseline_mixture(x, prior, wl, mout, n_queries, min_seconds=2.0, max_reps=10):
+    """The CPU reference of the mixture call on the first n_queries queries."""
+    from oracle import oracle
+    import numpy as np
+    xs = oracle.host_logits(x[:n_queries])
+    ps = prior[:n_queries].cpu().numpy()
+    times, m = [], None
+    while len(times) < max_reps and (sum(times) < min_seconds or len(times) < 2):
+        t0 = time.perf_counter()
+        m = oracle.mixture(xs, ps, k=wl.k)
+        oracle.mixture_tree(m["prior_w"].astype(np.float32), m["cand_count"], m["cand_tokens"],
+                            m["cand_p"].astype(np.float32), nmax=wl.nmax,
+                            row_status=m["row_status"])
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    ok = bool((mout["chain_tokens"][:n_queries].cpu().numpy() == m["chain_tokens"]).all())
+    return dict(value=n_queries / dt, unit="trees/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"first {n_queries} of {wl.B} queries of the timed batch "
+                       f"({n_queries * wl.K * wl.b} branch rows): float64 softmax + top-k, "
+                       f"chains and q_dep, candidate unions, mixture tree; median of "
+                       f"{len(times)} passes, {dt:.3f} s per pass"), ok
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -101,17 +128,30 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     binding.lib()
-    bufs = [synth.make_logits(wl, device=dev, seed=wl.seed + i) for i in range(N_BUFFERS)]
+    mixture = wl.K > 1
+    nbuf = 2 if mixture else N_BUFFERS
+    bufs = [synth.make_logits(wl, device=dev, seed=wl.seed + i) for i in range(nbuf)]
     cost = None
     if wl.online:
         c, _ = synth.make_cost_table(wl.B, wl.nmax, seed=wl.seed, **synth.LATENCY_A100)
         cost = torch.from_numpy(c).to(dev)
     ws = binding.Workspace(dev)
-    outs = [binding.alloc_tree_out(wl.B, wl.b, wl.k, wl.nmax, dev) for _ in range(N_BUFFERS)]
+    if mixture:
+        prior = synth.make_prior_logits(wl, device=dev)
+        mouts = [binding.alloc_mixture_out(wl.B, wl.K, wl.b, wl.k, dev) for _ in range(nbuf)]
+        outs = [binding.alloc_tree_out(wl.B, wl.b, wl.k, wl.nmax, dev, with_rows=False)
+                for _ in range(nbuf)]
+    else:
+        outs = [binding.alloc_tree_out(wl.B, wl.b, wl.k, wl.nmax, dev) for _ in range(nbuf)]
 
     def step(i):
-        binding.build_trees(bufs[i % N_BUFFERS], k=wl.k, nmax=wl.nmax, nmin=wl.nmin, cost=cost,
-                            out=outs[i % N_BUFFERS], ws=ws)
+        j = i % nbuf
+        if mixture:
+            binding.mixture_score(bufs[j], prior, k=wl.k, nmax=wl.nmax, out=mouts[j], tree=outs[j],
+                                  ws=ws)
+        else:
+            binding.build_trees(bufs[j], k=wl.k, nmax=wl.nmax, nmin=wl.nmin, cost=cost,
+                                out=outs[j], ws=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -132,6 +172,8 @@ def main():
 
     ms_per_step = wall * 1e3 / args.steps
     alg_bytes = wl.logit_bytes + out_bytes(outs[0])
+    if mixture:
+        alg_bytes += out_bytes(mouts[0]) + prior.numel() * 4
     mean_ms = float(launch_ms.mean())
     achieved = alg_bytes / (mean_ms * 1e-3) / 1e9
     traffic = None
@@ -153,10 +195,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}",
-                   "logits_dtype": wl.dtype, "rotating_buffers": N_BUFFERS},
+                   "logits_dtype": wl.dtype, "rotating_buffers": nbuf},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "build_trees_kernel", "alg_bytes_per_launch": alg_bytes,
+                     "kernel": "build_trees_kernel (mixture mode)" if mixture else "build_trees_kernel", "alg_bytes_per_launch": alg_bytes,
                      "launch_us_mean": mean_ms * 1e3,
                      "launch_us_p50": float(np.median(launch_ms)) * 1e3,
                      "launch_us_p10": float(np.percentile(launch_ms, 10)) * 1e3,
@@ -173,14 +215,19 @@ def main():
         line["calib_copy_bytes"] = n
     if not args.no_cpu_baseline:
         from oracle import oracle
-        x_host = oracle.host_logits(bufs[0])
-        n_q = wl.B
-        base, rows = cpu_baseline(x_host, wl, n_q)
-        line["cpu_baseline"] = base
-        # the timed GPU outputs of buffer 0 agree with the reference sample
-        g_ids = outs[0]["topk_ids"][:n_q].cpu().numpy()
-        line["parity_sample"] = {"queries": n_q,
-                                 "topk_ids_exact": bool((g_ids == rows["topk_ids"]).all())}
+        if mixture:
+            base, ok = cpu_baseline_mixture(bufs[0], prior, wl, mouts[0], n_queries=2)
+            line["cpu_baseline"] = base
+            line["parity_sample"] = {"queries": 2, "chain_tokens_exact": ok}
+        else:
+            x_host = oracle.host_logits(bufs[0])
+            n_q = wl.B
+            base, rows = cpu_baseline(x_host, wl, n_q)
+            line["cpu_baseline"] = base
+            # the timed GPU outputs of buffer 0 agree with the reference sample
+            g_ids = outs[0]["topk_ids"][:n_q].cpu().numpy()
+            line["parity_sample"] = {"queries": n_q,
+                                     "topk_ids_exact": bool((g_ids == rows["topk_ids"]).all())}
     print(json.dumps(line), flush=True)
 
 

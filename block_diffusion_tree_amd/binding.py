@@ -220,3 +220,49 @@ def accept(parent, token, n_nodes, b: int, target):
                                 _ptr(target), _ptr(alen), _ptr(anodes), _ptr(bonus), _stream()),
            "bastion_accept")
     return alen, anodes, bonus
+
+
+def alloc_mixture_out(B, K, b, k, device):
+    C_ = K * k
+    i32 = dict(dtype=torch.int32, device=device)
+    f32 = dict(dtype=torch.float32, device=device)
+    return dict(prior_q=torch.empty((B, K), **f32),
+                chain_tokens=torch.empty((B, K, b), **i32),
+                qdep_chain=torch.empty((B, K), dtype=torch.float64, device=device),
+                cand_count=torch.empty((B, b), **i32),
+                cand_tokens=torch.empty((B, b, C_), **i32),
+                cand_q=torch.empty((B, b, C_, K), **f32),
+                row_max=torch.empty((B, K, b), **f32),
+                row_sum=torch.empty((B, K, b), **f32))
+
+
+def mixture_score(branch_logits, prior_logits, k: int, nmax: int, with_tree: bool = True,
+                  with_mask: bool = True, out=None, tree=None, ws=None):
+    """bastion_mixture_score on branch logits [B, K, b, V] (float32 or bfloat16)
+    and prior logits [B, K] float32, on GPU.  Returns (mixture outputs, tree
+    outputs or None)."""
+    _dev(branch_logits, "branch_logits")
+    _dev(prior_logits, "prior_logits")
+    x = branch_logits
+    if x.dim() != 4 or x.stride(3) != 1 or x.stride(1) != x.size(2) * x.stride(2) \
+            or x.stride(0) != x.size(1) * x.stride(1):
+        raise ValueError("branch_logits must be [B, K, b, V] with unit stride over V and rows packed")
+    if prior_logits.dtype != torch.float32 or not prior_logits.is_contiguous():
+        raise TypeError("prior_logits must be a contiguous float32 GPU tensor")
+    B, K, b, V = x.shape
+    dt = _dtype_code(x)
+    if out is None:
+        out = alloc_mixture_out(B, K, b, k, x.device)
+    if with_tree and tree is None:
+        tree = alloc_tree_out(B, b, k, nmax, x.device, with_rows=False, with_mask=with_mask)
+    if not with_tree:
+        tree = None
+    L = lib()
+    w = _workspace(ws, x.device)
+    buf = w.get(L.bastion_workspace_bytes(B, K, b, V, k, nmax, dt))
+    mo = MixOut(*[_ptr(out[n]) for n, _ in MixOut._fields_])
+    ts = None if tree is None else C.byref(_tree_struct(tree))
+    _check(L.bastion_mixture_score(_ptr(x), dt, _ptr(prior_logits), B, K, b, V, x.stride(2), k,
+                                   nmax, C.byref(mo), ts, _ptr(buf), buf.numel(), _stream()),
+           "bastion_mixture_score")
+    return out, tree

@@ -9,6 +9,7 @@
 #include "device_common.hpp"
 
 #include "build_params.hpp"
+#include "mixture.hpp"
 
 // launchers, defined next to their kernels
 
@@ -44,7 +45,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int esize(int dtype) { return dtype == BASTION_BF16 ? 2 : 4; }
 
 struct Layout {
-    size_t row_status, partials, total;
+    size_t row_status, partials, row_ms, mtopk_ids, mtopk_q, total;
     int S;
 };
 
@@ -69,7 +70,11 @@ Layout layout(int64_t rows, int k, int S) {
     L.S = S;
     L.row_status = kTicketBytes;
     L.partials = align256(L.row_status + size_t(rows) * 4);
-    L.total = align256(L.partials + (S > 1 ? size_t(rows) * S * size_t(16 + 8 * k) : 0));
+    // row statistics and branch top-k of the latent-mixture call
+    L.row_ms = align256(L.partials + (S > 1 ? size_t(rows) * S * size_t(16 + 8 * k) : 0));
+    L.mtopk_ids = align256(L.row_ms + size_t(rows) * 8);
+    L.mtopk_q = align256(L.mtopk_ids + size_t(rows) * k * 4);
+    L.total = align256(L.mtopk_q + size_t(rows) * k * 4);
     return L;
 }
 
@@ -156,6 +161,11 @@ int32_t bastion_build_trees(const void *logits, int32_t dtype, int32_t B, int32_
     P.row_status = reinterpret_cast<int32_t *>(w + L.row_status);
     P.partials = w + L.partials;
     P.partial_bytes = 16 + 8 * k;
+    P.mode = 0;
+    P.K = 1;
+    P.rows_per_query = b;
+    P.is_bf16 = dtype == BASTION_BF16;
+    P.row_ms = nullptr;
     return to_status(bastion_launch_build(P, dtype, static_cast<hipStream_t>(stream), nullptr));
 }
 
@@ -194,10 +204,57 @@ int32_t bastion_mixture_score(const void *branch_logits, int32_t dtype, const fl
                               int32_t k, int32_t nmax, const bastion_mixture_out *mix,
                               const bastion_tree_out *tree, void *ws, size_t ws_bytes,
                               void *stream) {
-    (void)branch_logits; (void)dtype; (void)prior_logits; (void)B; (void)K; (void)b; (void)V;
-    (void)row_stride; (void)k; (void)nmax; (void)mix; (void)tree; (void)ws; (void)ws_bytes;
-    (void)stream;
-    return BASTION_EUNSUPPORTED;
+    if (!branch_logits || !prior_logits || (dtype != BASTION_F32 && dtype != BASTION_BF16))
+        return BASTION_EINVAL;
+    if (K < 1 || K > kMaxBranches || !sizes_ok(B, b, V, k, nmax)) return BASTION_EINVAL;
+    if (row_stride < V || (reinterpret_cast<uintptr_t>(branch_logits) % esize(dtype)) != 0)
+        return BASTION_EINVAL;
+    if (!mix || !mix->prior_q || !mix->chain_tokens || !mix->qdep_chain || !mix->cand_count ||
+        !mix->cand_tokens || !mix->cand_q || !mix->row_max || !mix->row_sum)
+        return BASTION_EINVAL;
+    if (tree && !tree_out_ok(tree, false)) return BASTION_EINVAL;
+    // the query stage keeps one position's candidates and the running list in LDS
+    if (mix_layout(K, b, k, nmax).total > 65536) return BASTION_EUNSUPPORTED;
+    const int64_t rows = int64_t(B) * K * b;
+    const int S = plan_segments(rows, V, dtype);
+    const Layout L = layout(rows, k, S);
+    if (!ws || !aligned16(ws) || ws_bytes < L.total) return BASTION_EWORKSPACE;
+
+    BuildParams P;
+    memset(&P, 0, sizeof P);
+    char *w = static_cast<char *>(ws);
+    P.logits = static_cast<const char *>(branch_logits);
+    P.row_stride_bytes = row_stride * esize(dtype);
+    P.B = B; P.b = b; P.V = V; P.k = k; P.nmax = nmax; P.nmin = 0; P.S = S;
+    P.cost = nullptr; P.cost_qstride = 0; P.l_ar = 1.0; P.pos_base = nullptr;
+    P.topk_ids = reinterpret_cast<int32_t *>(w + L.mtopk_ids);
+    P.topk_q = reinterpret_cast<float *>(w + L.mtopk_q);
+    P.row_max = mix->row_max;
+    P.row_sum = mix->row_sum;
+    if (tree) {
+        P.parent = tree->parent; P.depth = tree->depth; P.token = tree->token;
+        P.rho = tree->rho; P.ahat = tree->ahat; P.n_nodes = tree->n_nodes;
+        P.qstatus = tree->qstatus; P.mask = tree->mask; P.position_ids = tree->position_ids;
+    }
+    P.row_ticket = reinterpret_cast<uint32_t *>(w);
+    P.query_ticket = reinterpret_cast<uint32_t *>(w) + kQueryTicketBase;
+    P.row_status = reinterpret_cast<int32_t *>(w + L.row_status);
+    P.partials = w + L.partials;
+    P.partial_bytes = 16 + 8 * k;
+    P.mode = 1;
+    P.K = K;
+    P.rows_per_query = K * b;
+    P.is_bf16 = dtype == BASTION_BF16;
+    P.row_ms = reinterpret_cast<float *>(w + L.row_ms);
+    P.prior = prior_logits;
+    P.prior_q = mix->prior_q;
+    P.chain_tokens = mix->chain_tokens;
+    P.qdep = mix->qdep_chain;
+    P.cand_count = mix->cand_count;
+    P.cand_tokens = mix->cand_tokens;
+    P.cand_q = mix->cand_q;
+    P.mix_tree = tree ? 1 : 0;
+    return to_status(bastion_launch_build(P, dtype, static_cast<hipStream_t>(stream), nullptr));
 }
 
 }  // extern "C"

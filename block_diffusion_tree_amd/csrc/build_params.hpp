@@ -26,6 +26,19 @@ struct BuildParams {
     int32_t *row_status;
     char *partials;       // [rows, S] records of kPartialBytes(k)
     int partial_bytes;
+    // latent mixture (mode 1): rows are ((q*K + z)*b + i)
+    int mode;             // 0: trees over [B, b, V]; 1: mixture over [B, K, b, V]
+    int K;
+    int rows_per_query;   // b, or K * b
+    int is_bf16;
+    float *row_ms;        // [rows, 2] row max and internal sum, or NULL
+    const float *prior;   // [B, K]
+    float *prior_q;       // [B, K]
+    int32_t *chain_tokens;
+    double *qdep;
+    int32_t *cand_count, *cand_tokens;
+    float *cand_q;
+    int mix_tree;         // 1: build the mixture tree into parent/depth/...
 };
 
 }  // namespace bastion

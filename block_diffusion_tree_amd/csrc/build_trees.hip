@@ -16,6 +16,7 @@
 #include "build_params.hpp"
 #include "tree_rounds.hpp"
 #include "tree_pool.hpp"
+#include "mixture.hpp"
 
 namespace bastion {
 
@@ -483,6 +484,103 @@ __device__ int exact_build(const RoundsLds &S, int b, int k, int nmax) {
     return cnt;
 }
 
+// A_hat[n] = 1 + rho[1] + ... + rho[n], float64, n = 1..cnt (one wave; rho
+// and ahat in LDS, pop order).
+__device__ void ahat_fill(const float *rho, double *ahat, int cnt) {
+    const int lane = lane_id();
+    // A_hat: float64 running sum in pop order (the order best-first adds).
+    // When the smallest rho is at least 2^(L-30), with 2^L > cnt + 1,
+    // every rho is a multiple of ulp(smallest) and every partial sum is
+    // below 2^L, so all sums are exact in float64 and a parallel scan
+    // gives the same bits as the running sum.
+    const uint32_t rb = cnt >= 1 ? __float_as_uint(rho[cnt]) : 0u;
+    const int Lb = 32 - __clz(cnt + 1);
+    const bool exact = cnt >= 1 && (rb >> 23) != 0u && int(rb >> 23) - 127 >= Lb - 30;
+    if (exact) {
+        double carry = 1.0;
+        for (int c0 = 0; c0 < cnt; c0 += kWave) {
+            const int n = c0 + 1 + lane;
+            double v = n <= cnt ? double(rho[n]) : 0.0;
+#pragma unroll
+            for (int sft = 1; sft < kWave; sft <<= 1) {
+                const double o = __shfl_up(v, sft);
+                v += lane >= sft ? o : 0.0;
+            }
+            if (n <= cnt) ahat[n] = carry + v;
+            carry += __shfl(v, kWave - 1);
+        }
+    } else if (lane == 0) {
+        double ah = 1.0;
+        int n = 1;
+        for (; n + 8 <= cnt + 1; n += 8) {
+            float r[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) r[i] = rho[n + i];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                ah += double(r[i]);
+                ahat[n + i] = ah;
+            }
+        }
+        for (; n <= cnt; ++n) {
+            ah += double(rho[n]);
+            ahat[n] = ah;
+        }
+    }
+    wave_sync();
+}
+
+// Pop-order outputs of one query (records 1..nstar in par/dep/tok/rho/ahat,
+// LDS), padding, n_nodes, qstatus and, when requested, the ancestor mask and
+// position ids (whole block).
+__device__ void emit_tree(const BuildParams &P, int q, const int32_t *par, const int32_t *dep,
+                          const int32_t *tok, const float *rho, const double *ahat, int nstar,
+                          bool bad, int status) {
+    const int tid = threadIdx.x, nmax = P.nmax, b = P.b;
+    const int W1 = nmax + 1;
+    const int64_t o = int64_t(q) * W1;
+    for (int i = tid; i < W1; i += kThreads) {
+        const bool v = i <= nstar && !bad;
+        P.parent[o + i] = v ? (i == 0 ? -1 : par[i]) : -1;
+        P.depth[o + i] = v ? (i == 0 ? 0 : dep[i]) : -1;
+        P.token[o + i] = v ? (i == 0 ? -1 : tok[i]) : -1;
+        P.rho[o + i] = v ? (i == 0 ? 1.0f : rho[i]) : 0.0f;
+        P.ahat[o + i] = v ? (i == 0 ? 1.0 : ahat[i]) : 0.0;
+    }
+    if (bad && tid == 0) {
+        P.parent[o] = -1;
+        P.depth[o] = 0;
+        P.token[o] = -1;
+        P.rho[o] = 1.0f;
+        P.ahat[o] = 1.0;
+    }
+    if (tid == 0) {
+        P.n_nodes[q] = nstar;
+        P.qstatus[q] = status;
+    }
+    if (P.mask) {
+        // one thread per (node, mask word), each walking up from the node
+        const int W = (W1 + 31) / 32;
+        const int32_t pb = P.pos_base ? P.pos_base[q] : 0;
+        for (int e = tid; e < W1 * W; e += kThreads) {
+            const int i = e / W, w = e - i * W;
+            uint32_t bits = 0;
+            int steps = 0;
+            if (i <= nstar) {
+                int j = i;
+                if (j / 32 == w) bits |= 1u << (j & 31);
+                while (j > 0 && steps < b) {
+                    j = par[j];
+                    ++steps;
+                    if (j / 32 == w) bits |= 1u << (j & 31);
+                }
+            }
+            P.mask[(o + i) * W + w] = bits;
+            if (w == 0) P.position_ids[o + i] = i <= nstar ? pb + steps : -1;
+        }
+    }
+}
+
 template <int G>
 __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -560,46 +658,7 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
             S.ahat[0] = 1.0;
         }
         wave_sync();
-        // A_hat: float64 running sum in pop order (the order best-first adds).
-        // When the smallest rho is at least 2^(L-30), with 2^L > cnt + 1,
-        // every rho is a multiple of ulp(smallest) and every partial sum is
-        // below 2^L, so all sums are exact in float64 and a parallel scan
-        // gives the same bits as the running sum.
-        const uint32_t rb = cnt >= 1 ? __float_as_uint(S.rho[cnt]) : 0u;
-        const int Lb = 32 - __clz(cnt + 1);
-        const bool exact = cnt >= 1 && (rb >> 23) != 0u && int(rb >> 23) - 127 >= Lb - 30;
-        if (exact) {
-            double carry = 1.0;
-            for (int c0 = 0; c0 < cnt; c0 += kWave) {
-                const int n = c0 + 1 + lane;
-                double v = n <= cnt ? double(S.rho[n]) : 0.0;
-#pragma unroll
-                for (int sft = 1; sft < kWave; sft <<= 1) {
-                    const double o = __shfl_up(v, sft);
-                    v += lane >= sft ? o : 0.0;
-                }
-                if (n <= cnt) S.ahat[n] = carry + v;
-                carry += __shfl(v, kWave - 1);
-            }
-        } else if (lane == 0) {
-            double ah = 1.0;
-            int n = 1;
-            for (; n + 8 <= cnt + 1; n += 8) {
-                float r[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) r[i] = S.rho[n + i];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    ah += double(r[i]);
-                    S.ahat[n + i] = ah;
-                }
-            }
-            for (; n <= cnt; ++n) {
-                ah += double(S.rho[n]);
-                S.ahat[n] = ah;
-            }
-        }
-        wave_sync();
+        ahat_fill(S.rho, S.ahat, cnt);
         int nstar = cnt;
         if (online) {
             // the first n >= nmin with S(n+1) < S(n)
@@ -626,48 +685,186 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
     __syncthreads();
     const int nstar = bad ? 0 : s_nstar;
     const int status = bad ? BASTION_Q_BAD_LOGITS : s_status;
-    const int W1 = nmax + 1;
-    const int64_t o = int64_t(q) * W1;
-    for (int i = tid; i < W1; i += kThreads) {
-        const bool v = i <= nstar && !bad;
-        P.parent[o + i] = v ? (i == 0 ? -1 : S.par[i]) : -1;
-        P.depth[o + i] = v ? (i == 0 ? 0 : S.dep[i]) : -1;
-        P.token[o + i] = v ? (i == 0 ? -1 : S.tok[i]) : -1;
-        P.rho[o + i] = v ? (i == 0 ? 1.0f : S.rho[i]) : 0.0f;
-        P.ahat[o + i] = v ? (i == 0 ? 1.0 : S.ahat[i]) : 0.0;
-    }
-    if (bad && tid == 0) {
-        P.parent[o] = -1;
-        P.depth[o] = 0;
-        P.token[o] = -1;
-        P.rho[o] = 1.0f;
-        P.ahat[o] = 1.0;
+    emit_tree(P, q, S.par, S.dep, S.tok, S.rho, S.ahat, nstar, bad, status);
+}
+
+// Latent-mixture stage of one query (mixture.hpp): prior weights, chains and
+// their q_dep, candidate unions with q per branch, and the mixture tree.
+__device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int K = P.K, b = P.b, k = P.k, C = K * k, nmax = P.nmax;
+    const MixLds M = mix_lds(smem, mix_layout(K, b, k, nmax));
+    const int64_t r0 = int64_t(q) * K * b;
+    __shared__ int s_bad, s_cnt, s_ns, s_np;
+    __shared__ uint64_t s_tau;
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+    for (int e = tid; e < K * b; e += kThreads) {
+        M.rowm[e] = ld_agent(P.row_ms + 2 * (r0 + e));
+        M.rows[e] = ld_agent(P.row_ms + 2 * (r0 + e) + 1);
+        if (ld_agent(P.row_status + r0 + e) != BASTION_Q_OK) atomicOr(&s_bad, 1);
     }
     if (tid == 0) {
-        P.n_nodes[q] = nstar;
-        P.qstatus[q] = status;
-    }
-    if (P.mask) {
-        // one thread per (node, mask word), each walking up from the node
-        const int W = (W1 + 31) / 32;
-        const int32_t pb = P.pos_base ? P.pos_base[q] : 0;
-        for (int e = tid; e < W1 * W; e += kThreads) {
-            const int i = e / W, w = e - i * W;
-            uint32_t bits = 0;
-            int steps = 0;
-            if (i <= nstar) {
-                int j = i;
-                if (j / 32 == w) bits |= 1u << (j & 31);
-                while (j > 0 && steps < b) {
-                    j = S.par[j];
-                    ++steps;
-                    if (j / 32 == w) bits |= 1u << (j & 31);
-                }
-            }
-            P.mask[(o + i) * W + w] = bits;
-            if (w == 0) P.position_ids[o + i] = i <= nstar ? pb + steps : -1;
+        // prior weights, float64 softmax
+        double pm = -INFINITY, ps = 0.0;
+        for (int z = 0; z < K; ++z) pm = fmax(pm, double(P.prior[q * K + z]));
+        for (int z = 0; z < K; ++z) ps += exp(double(P.prior[q * K + z]) - pm);
+        for (int z = 0; z < K; ++z) {
+            const double w = exp(double(P.prior[q * K + z]) - pm) / ps;
+            M.w[z] = w;
+            M.wq[z] = float(w);
+            P.prior_q[q * K + z] = float(w);
         }
     }
+    __syncthreads();
+    const int64_t cbase = int64_t(q) * b * C;
+    if (s_bad) {
+        // a bad branch row: no chains, no candidates, the root alone
+        for (int e = tid; e < K * b; e += kThreads) P.chain_tokens[r0 + e] = -1;
+        for (int z = tid; z < K; z += kThreads) P.qdep[q * K + z] = 0.0;
+        for (int e = tid; e < b * C; e += kThreads) P.cand_tokens[cbase + e] = -1;
+        for (int e = tid; e < b * C * K; e += kThreads) P.cand_q[cbase * K + e] = 0.0f;
+        for (int i = tid; i < b; i += kThreads) P.cand_count[int64_t(q) * b + i] = 0;
+        if (P.mix_tree) emit_tree(P, q, M.par, M.dep, M.tok, M.rho, M.ahat, 0, true, BASTION_Q_BAD_LOGITS);
+        return;
+    }
+    // chains: the top-1 token of every branch row
+    for (int e = tid; e < K * b; e += kThreads) {
+        const int t = ld_agent(P.topk_ids + (r0 + e) * k);
+        M.chain[e] = t;
+        P.chain_tokens[r0 + e] = t;
+    }
+    __syncthreads();
+    // q_dep: thread (z, z') forms prod_i q_i(chain z | z') in float64
+    for (int t = tid; t < K * K; t += kThreads) {
+        const int z = t / K, zp = t - z * K;
+        double pr = 1.0;
+        for (int i = 0; i < b; ++i) {
+            const int lr = zp * b + i;
+            const float l = mix_logit(P, r0 + lr, M.chain[z * b + i], P.is_bf16);
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(l, kLog2e, -scale_ref(M.rowm[lr])));
+            pr *= double(e / M.rows[lr]);
+        }
+        M.prod[t] = pr;
+    }
+    __syncthreads();
+    for (int z = tid; z < K; z += kThreads) {
+        double qd = 0.0;
+        for (int zp = 0; zp < K; ++zp) qd += M.w[zp] * M.prod[z * K + zp];
+        P.qdep[q * K + z] = qd;
+    }
+    // candidates and the tree, position by position
+    int nR = 0;
+    bool grow = P.mix_tree != 0;
+    for (int d = 1; d <= b; ++d) {
+        const int pos = d - 1;
+        if (tid == 0) s_cnt = 0;
+        for (int c = tid; c < C; c += kThreads) {
+            const int z = c / k, j = c - z * k;
+            M.ids[c] = ld_agent(P.topk_ids + (r0 + z * b + pos) * k + j);
+        }
+        __syncthreads();
+        // first occurrences, then their ascending ranks
+        for (int c = tid; c < C; c += kThreads) {
+            const int t = M.ids[c];
+            int f = 1;
+            for (int c2 = 0; c2 < c; ++c2) f = (M.ids[c2] == t) ? 0 : f;
+            M.first[c] = f;
+        }
+        __syncthreads();
+        for (int c = tid; c < C; c += kThreads) {
+            if (M.first[c]) {
+                const int t = M.ids[c];
+                int r = 0;
+                for (int c2 = 0; c2 < C; ++c2) r += (M.first[c2] && M.ids[c2] < t) ? 1 : 0;
+                M.ctok[r] = t;
+                atomicAdd(&s_cnt, 1);
+            }
+        }
+        __syncthreads();
+        const int cnt = s_cnt;
+        int32_t *ct_out = P.cand_tokens + cbase + int64_t(pos) * C;
+        for (int c = tid; c < C; c += kThreads) ct_out[c] = c < cnt ? M.ctok[c] : -1;
+        if (tid == 0) P.cand_count[int64_t(q) * b + pos] = cnt;
+        // q of every candidate in every branch (the row's own top-k formula)
+        float *cq_out = P.cand_q + (cbase + int64_t(pos) * C) * K;
+        for (int e = tid; e < C * K; e += kThreads) {
+            const int c = e / K, z = e - c * K;
+            float v = 0.0f;
+            if (c < cnt) {
+                const int lr = z * b + pos;
+                const float l = mix_logit(P, r0 + lr, M.ctok[c], P.is_bf16);
+                v = __builtin_amdgcn_exp2f(__builtin_fmaf(l, kLog2e, -scale_ref(M.rowm[lr]))) / M.rows[lr];
+                M.cq[e] = v;
+            }
+            cq_out[e] = v;
+        }
+        __syncthreads();
+        if (!grow) continue;
+        // tree round d: the parents are the depth-(d-1) entries, in order
+        if (d == 1) {
+            if (tid < K) M.ptab[tid] = 1.0f;
+            if (tid == 0) s_np = 1;
+        } else if (wv == 0) {
+            const uint64_t lt = lanemask_lt();
+            int np = 0;
+            for (int e0 = 0; e0 < nR; e0 += kWave) {
+                const int e = e0 + lane;
+                const bool v = e < nR && tree_key_depth(M.rkey[e]) == d - 1;
+                const uint64_t m = __ballot(v);
+                if (v) {
+                    const int pp = np + popc64(m & lt);
+                    for (int z = 0; z < K; ++z) M.ptab[pp * K + z] = M.rr[e * K + z];
+                }
+                np += popc64(m);
+            }
+            if (lane == 0) s_np = np;
+        }
+        if (tid == 0) {
+            s_ns = 0;
+            s_tau = nR == nmax ? M.rkey[nmax - 1] : 0;
+        }
+        __syncthreads();
+        const int np = s_np;
+        if (np == 0) {
+            grow = false;
+            continue;
+        }
+        const int total = np * cnt;
+        for (int base = 0; base < total; base += kThreads) {
+            const int idx = base + tid;
+            if (idx < total) {
+                const int p = idx / cnt, c = idx - p * cnt;
+                const float score = mix_child(M, K, p, c);
+                const uint64_t key = tree_key(score, d, M.ctok[c], p);
+                if (key > s_tau) {
+                    const int slot = atomicAdd(&s_ns, 1);
+                    M.skey[slot] = key;
+                    M.sinfo[slot] = (p << 16) | c;
+                }
+            }
+            __syncthreads();
+            const int ns = s_ns;
+            // merge when the buffer could not take another chunk, at the end
+            // of the round, and while the list is not full (to set its N-th key)
+            if (ns > 0 && (ns > kMixSurv - kThreads || base + kThreads >= total || nR < nmax)) {
+                nR = mix_merge<kThreads>(M, K, nmax, nR, ns);
+                if (tid == 0) {
+                    s_ns = 0;
+                    s_tau = nR == nmax ? M.rkey[nmax - 1] : 0;
+                }
+                __syncthreads();
+            }
+        }
+    }
+    if (!P.mix_tree) return;
+    if (wv == 0) {
+        mix_resolve(M, b, nmax, nR);
+        ahat_fill(M.rho, M.ahat, nR);
+    }
+    __syncthreads();
+    emit_tree(P, q, M.par, M.dep, M.tok, M.rho, M.ahat, nR, false,
+              nR < nmax ? BASTION_Q_EXHAUSTED : BASTION_Q_OK);
 }
 
 // ---------------------------------------------------------------------------
@@ -675,12 +872,13 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
 // ---------------------------------------------------------------------------
 constexpr int partial_bytes(int k) { return 16 + 8 * k; }
 
-template <typename T, int U, int R>
+// MODE 0: trees (tree_stage with R registers); MODE 1: latent mixture.
+template <typename T, int U, int R, int MODE>
 __global__ __launch_bounds__(kThreads, (R >= 16 ? 2 : 4)) void build_trees_kernel(BuildParams P) {
     extern __shared__ __align__(16) char smem[];
     const int row = blockIdx.x / P.S;
     const int seg = blockIdx.x - row * P.S;
-    const int q = row / P.b;
+    const int q = row / P.rows_per_query;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const char *rowp = P.logits + int64_t(row) * P.row_stride_bytes;
 
@@ -763,19 +961,24 @@ __global__ __launch_bounds__(kThreads, (R >= 16 ? 2 : 4)) void build_trees_kerne
             P.row_max[row] = badrow ? 0.0f : M;
             P.row_sum[row] = badrow ? 0.0f : Ssum * __builtin_amdgcn_exp2f(-d);
             st_agent(P.row_status + row, int32_t(badrow ? BASTION_Q_BAD_LOGITS : BASTION_Q_OK));
+            if (P.row_ms) {
+                st_agent(P.row_ms + 2 * row, M);
+                st_agent(P.row_ms + 2 * row + 1, Ssum);
+            }
         }
     }
-    if (!arrive_last(P.query_ticket + q, uint32_t(P.b))) return;
-    tree_stage<R>(P, q, smem);
+    if (!arrive_last(P.query_ticket + q, uint32_t(P.rows_per_query))) return;
+    if constexpr (MODE == 1) mixture_stage(P, q, smem);
+    else tree_stage<R>(P, q, smem);
 }
 
 // ---------------------------------------------------------------------------
 // Host-side launch helpers (called from api.hip).
 // ---------------------------------------------------------------------------
-template <typename T, int U, int R>
+template <typename T, int U, int R, int MODE = 0>
 static hipError_t launch_one(const BuildParams &P, int smem, hipStream_t s) {
-    auto kern = build_trees_kernel<T, U, R>;
-    const int64_t grid = int64_t(P.B) * P.b * P.S;
+    auto kern = build_trees_kernel<T, U, R, MODE>;
+    const int64_t grid = int64_t(P.B) * P.rows_per_query * P.S;
     hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), smem, s, P);
     return hipGetLastError();
 }
@@ -783,6 +986,7 @@ static hipError_t launch_one(const BuildParams &P, int smem, hipStream_t s) {
 template <typename T, int U>
 static hipError_t launch_r(const BuildParams &P, int smem, hipStream_t s) {
     // the running top-N list holds nmax keys in tree_regs(nmax) registers
+    if (P.mode == 1) return launch_one<T, U, 1, 1>(P, smem, s);
     switch (tree_regs(P.nmax)) {
         case 1: return launch_one<T, U, 1>(P, smem, s);
         case 2: return launch_one<T, U, 2>(P, smem, s);
@@ -800,7 +1004,8 @@ hipError_t bastion_launch_build(const bastion::BuildParams &P, int dtype, hipStr
     using namespace bastion;
     constexpr int U = 4;
     const int stream_smem = int(sizeof(WaveScratch<U>)) * kWavesPerBlock;
-    const int tree_smem = tree_layout(P.b, P.k, P.nmax).total;
+    const int tree_smem = P.mode == 1 ? mix_layout(P.K, P.b, P.k, P.nmax).total
+                                      : tree_layout(P.b, P.k, P.nmax).total;
     const int smem = stream_smem > tree_smem ? stream_smem : tree_smem;
     if (smem_out) *smem_out = smem;
     if (dtype == BASTION_BF16) return launch_r<__bf16, U>(P, smem, s);

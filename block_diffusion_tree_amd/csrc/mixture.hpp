@@ -1,0 +1,205 @@
+// mixture.hpp -- the latent-mixture stage for one query (DBlast, Methodology
+// 1 on the gist.science page: q_dep(x_1:b | y) = sum_z q(z|y) prod_i
+// q_i(x_i | y, z); a branch is decoded greedily), run by the block that
+// finishes the query's last branch row.
+//
+//   1. prior weights w = softmax(prior logits), float64 (stored as float32);
+//   2. chain z = the top-1 token of every position of branch z;
+//      q_dep(chain z) = sum_z' w_z' prod_i q_i(x_i | z'), float64, each q
+//      from the branch row's max and sum at the chain token (logit gather);
+//   3. per position, the union of the branches' top-k tokens in ascending
+//      order and q_i(token | z) for every branch (float32, the same formula
+//      as the row's own top-k q);
+//   4. when asked, the best-first tree over those candidates.  A node keeps
+//      r_z = fl32 product of q_i(x_i | z) along its path and is scored by the
+//      float32 fma chain sum_z w_z r_z; children score no higher than their
+//      parent, so the level-synchronous argument of the plain tree holds:
+//      after round d the running list holds the N best nodes of depth <= d,
+//      round d merging the children of its depth-(d-1) nodes.  A child's key
+//      carries its parent's rank among the depth-(d-1) entries, which is
+//      best-first's parent-order tie-break.  Candidates that beat the list's
+//      N-th key are buffered and merged kMixSurv at a time.
+#pragma once
+
+#include "device_common.hpp"
+#include "build_params.hpp"
+
+namespace bastion {
+
+constexpr int kMixSurv = 512;   // survivors buffered between merges
+
+struct MixLayout {
+    int w, wq, prod, rowm, rows, chain, ids, first, ctok, cq, rkey, rr, nkey, nr, ptab, skey, sinfo, map,
+        base, par, dep, tok, rho, ahat, total;
+};
+
+__host__ __device__ inline int mix_align16(int x) { return (x + 15) & ~15; }
+
+__host__ __device__ inline MixLayout mix_layout(int K, int b, int k, int nmax) {
+    MixLayout L;
+    const int C = K * k, nn = nmax + 2;
+    int o = 0;
+    L.w = o;     o = mix_align16(o + 8 * K);
+    L.wq = o;    o = mix_align16(o + 4 * K);
+    L.prod = o;  o = mix_align16(o + 8 * K * K);
+    L.rowm = o;  o = mix_align16(o + 4 * K * b);
+    L.rows = o;  o = mix_align16(o + 4 * K * b);
+    L.chain = o; o = mix_align16(o + 4 * K * b);
+    L.ids = o;   o = mix_align16(o + 4 * C);
+    L.first = o; o = mix_align16(o + 4 * C);
+    L.ctok = o;  o = mix_align16(o + 4 * C);
+    L.cq = o;    o = mix_align16(o + 4 * C * K);
+    L.rkey = o;  o = mix_align16(o + 8 * nmax);
+    L.rr = o;    o = mix_align16(o + 4 * nmax * K);
+    L.nkey = o;  o = mix_align16(o + 8 * nmax);
+    L.nr = o;    o = mix_align16(o + 4 * nmax * K);
+    L.ptab = o;  o = mix_align16(o + 4 * nmax * K);
+    L.skey = o;  o = mix_align16(o + 8 * kMixSurv);
+    L.sinfo = o; o = mix_align16(o + 4 * kMixSurv);
+    L.map = o;   o = mix_align16(o + 4 * nn);
+    L.base = o;  o = mix_align16(o + 4 * 40);
+    L.par = o;   o = mix_align16(o + 4 * nn);
+    L.dep = o;   o = mix_align16(o + 4 * nn);
+    L.tok = o;   o = mix_align16(o + 4 * nn);
+    L.rho = o;   o = mix_align16(o + 4 * nn);
+    L.ahat = o;  o = mix_align16(o + 8 * nn);
+    L.total = o;
+    return L;
+}
+
+struct MixLds {
+    double *w, *prod;
+    float *wq, *rowm, *rows, *cq, *rr, *nr, *ptab;
+    int32_t *chain, *ids, *first, *ctok, *sinfo, *map, *base, *par, *dep, *tok;
+    uint64_t *rkey, *nkey, *skey;
+    float *rho;
+    double *ahat;
+};
+
+__device__ __forceinline__ MixLds mix_lds(char *smem, const MixLayout &L) {
+    MixLds M;
+    M.w = reinterpret_cast<double *>(smem + L.w);
+    M.wq = reinterpret_cast<float *>(smem + L.wq);
+    M.prod = reinterpret_cast<double *>(smem + L.prod);
+    M.rowm = reinterpret_cast<float *>(smem + L.rowm);
+    M.rows = reinterpret_cast<float *>(smem + L.rows);
+    M.chain = reinterpret_cast<int32_t *>(smem + L.chain);
+    M.ids = reinterpret_cast<int32_t *>(smem + L.ids);
+    M.first = reinterpret_cast<int32_t *>(smem + L.first);
+    M.ctok = reinterpret_cast<int32_t *>(smem + L.ctok);
+    M.cq = reinterpret_cast<float *>(smem + L.cq);
+    M.rkey = reinterpret_cast<uint64_t *>(smem + L.rkey);
+    M.rr = reinterpret_cast<float *>(smem + L.rr);
+    M.nkey = reinterpret_cast<uint64_t *>(smem + L.nkey);
+    M.nr = reinterpret_cast<float *>(smem + L.nr);
+    M.ptab = reinterpret_cast<float *>(smem + L.ptab);
+    M.skey = reinterpret_cast<uint64_t *>(smem + L.skey);
+    M.sinfo = reinterpret_cast<int32_t *>(smem + L.sinfo);
+    M.map = reinterpret_cast<int32_t *>(smem + L.map);
+    M.base = reinterpret_cast<int32_t *>(smem + L.base);
+    M.par = reinterpret_cast<int32_t *>(smem + L.par);
+    M.dep = reinterpret_cast<int32_t *>(smem + L.dep);
+    M.tok = reinterpret_cast<int32_t *>(smem + L.tok);
+    M.rho = reinterpret_cast<float *>(smem + L.rho);
+    M.ahat = reinterpret_cast<double *>(smem + L.ahat);
+    return M;
+}
+
+// fma-chain score of the child of parent p with candidate c: its r_z are
+// fl32(r_z(parent) * q(c | z))
+__device__ __forceinline__ float mix_child(const MixLds &M, int K, int p, int c) {
+    float acc = 0.0f;
+    for (int z = 0; z < K; ++z)
+        acc = __builtin_fmaf(M.wq[z], __fmul_rn(M.ptab[p * K + z], M.cq[c * K + z]), acc);
+    return acc;
+}
+
+// Merge the ns buffered survivors into the running list (nR sorted keys, at
+// most nmax): every element counts the larger keys; the count is its new
+// place.  Whole block.  Returns the new nR.
+template <int THREADS>
+__device__ int mix_merge(const MixLds &M, int K, int nmax, int nR, int ns) {
+    const int tid = threadIdx.x;
+    const int nE = nR + ns;
+    for (int e = tid; e < nE; e += THREADS) {
+        const uint64_t x = e < nR ? M.rkey[e] : M.skey[e - nR];
+        int rank;
+        if (e < nR) {
+            rank = e;
+        } else {
+            // larger keys of the sorted list: binary search
+            int lo = 0, hi = nR;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (M.rkey[mid] > x) lo = mid + 1;
+                else hi = mid;
+            }
+            rank = lo;
+        }
+        for (int s = 0; s < ns; ++s) rank += M.skey[s] > x ? 1 : 0;
+        if (rank < nmax) {
+            M.nkey[rank] = x;
+            if (e < nR) {
+                for (int z = 0; z < K; ++z) M.nr[rank * K + z] = M.rr[e * K + z];
+            } else {
+                const int info = M.sinfo[e - nR];
+                const int p = info >> 16, c = info & 0xFFFF;
+                for (int z = 0; z < K; ++z)
+                    M.nr[rank * K + z] = __fmul_rn(M.ptab[p * K + z], M.cq[c * K + z]);
+            }
+        }
+    }
+    __syncthreads();
+    const int n = nE < nmax ? nE : nmax;
+    for (int i = tid; i < n; i += THREADS) {
+        M.rkey[i] = M.nkey[i];
+        for (int z = 0; z < K; ++z) M.rr[i * K + z] = M.nr[i * K + z];
+    }
+    __syncthreads();
+    return n;
+}
+
+__device__ __forceinline__ float mix_logit(const BuildParams &P, int64_t row, int token,
+                                           int is_bf16) {
+    const char *p = P.logits + row * P.row_stride_bytes;
+    if (is_bf16) return float(reinterpret_cast<const __bf16 *>(p)[token]);
+    return reinterpret_cast<const float *>(p)[token];
+}
+
+// Pop-order tree records 1..cnt from the sorted running list (one wave).
+__device__ inline void mix_resolve(const MixLds &M, int b, int nmax, int cnt) {
+    const int lane = lane_id();
+    const uint64_t lt = lanemask_lt();
+    int basev = 0;
+    for (int d = 1; d <= b; ++d) {
+        if (lane == 0) M.base[d] = basev;
+        for (int e0 = 0; e0 < cnt; e0 += kWave) {
+            const int e = e0 + lane;
+            const bool v = e < cnt && tree_key_depth(M.rkey[e]) == d;
+            const uint64_t m = __ballot(v);
+            if (v) M.map[basev + popc64(m & lt)] = e + 1;
+            basev += popc64(m);
+        }
+    }
+    wave_sync();
+    for (int e = lane; e < cnt; e += kWave) {
+        const uint64_t key = M.rkey[e];
+        const int d = tree_key_depth(key);
+        int mi = M.base[d - 1] + tree_key_parent(key);
+        mi = mi < nmax ? mi : nmax;
+        M.par[e + 1] = d == 1 ? 0 : M.map[mi];
+        M.dep[e + 1] = d;
+        M.tok[e + 1] = tree_key_token(key);
+        M.rho[e + 1] = tree_key_rho(key);
+    }
+    if (lane == 0) {
+        M.par[0] = -1;
+        M.dep[0] = 0;
+        M.tok[0] = -1;
+        M.rho[0] = 1.0f;
+        M.ahat[0] = 1.0;
+    }
+    wave_sync();
+}
+
+}  // namespace bastion

@@ -95,6 +95,43 @@ def test_small_kernels_reject_bad_arguments(L):
     assert L.bastion_accept(FAKE, FAKE, FAKE, 2, 4, 8, None, FAKE, FAKE, FAKE, None) == 1
 
 
+def full_mix(**nulls):
+    from block_diffusion_tree_amd.binding import MixOut
+    vals = {n: FAKE for n, _ in MixOut._fields_}
+    vals.update(nulls)
+    return MixOut(**vals)
+
+
+def call_mix(L, logits=FAKE, dtype=1, prior=FAKE, B=2, K=4, b=4, V=1000, stride=1000, k=8,
+             nmax=16, mix=None, tree="full", ws=FAKE, ws_bytes=1 << 30):
+    mix = full_mix() if mix is None else mix
+    t = full_out() if tree == "full" else tree
+    return L.bastion_mixture_score(logits, dtype, prior, B, K, b, V, stride, k, nmax,
+                                   C.byref(mix), None if t is None else C.byref(t), ws,
+                                   ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(logits=None), dict(prior=None), dict(dtype=2), dict(K=0), dict(K=17), dict(B=0),
+    dict(b=33), dict(k=0), dict(k=33), dict(nmax=0), dict(nmax=1024), dict(stride=999),
+    dict(mix=None, tree=None, logits=None),
+])
+def test_mixture_rejects_bad_arguments(L, kw):
+    assert call_mix(L, **kw) == 1
+
+
+def test_mixture_rejects_incomplete_outputs_and_workspace(L):
+    assert call_mix(L, mix=full_mix(cand_q=None)) == 1
+    assert call_mix(L, mix=full_mix(qdep_chain=None)) == 1
+    assert call_mix(L, tree=full_out(rho=None)) == 1
+    need = L.bastion_workspace_bytes(2, 4, 4, 1000, 8, 16, 1)
+    assert call_mix(L, ws_bytes=need - 1) == 4
+    assert call_mix(L, tree=None, ws=None) == 4
+    # the mixture tree keeps one position's candidates in LDS: K = 16, k = 32
+    # and a large budget do not fit
+    assert call_mix(L, K=16, k=32, nmax=1000, V=1000) == 2
+
+
 def test_no_shared_code_between_library_and_reference():
     pkg = os.path.join(ROOT, "block_diffusion_tree_amd")
     for dirpath, _, files in os.walk(pkg):
