@@ -16,6 +16,7 @@
 #include "build_params.hpp"
 #include "tree_rounds.hpp"
 #include "tree_pool.hpp"
+#include "tree_family.hpp"
 #include "mixture.hpp"
 
 namespace bastion {
@@ -409,7 +410,7 @@ __host__ __device__ inline int tree_regs(int nmax) {
 
 struct TreeLayout {
     int qtab, ttab, col, par, dep, tok, rho, ahat, cost, map, base;
-    int pkey, ppar, prho, plrank, ppop, hist, plvl, q0col, total;
+    int pkey, ppar, prho, plrank, ppop, hist, plvl, q0col, fwork, total;
 };
 
 __host__ __device__ inline TreeLayout tree_layout(int b, int k, int nmax) {
@@ -428,14 +429,18 @@ __host__ __device__ inline TreeLayout tree_layout(int b, int k, int nmax) {
     L.cost = o; o = align16(o + 8 * nn);
     L.map = o;  o = align16(o + 4 * nn);
     L.base = o; o = align16(o + 4 * 40);
-    L.pkey = o; o = align16(o + 8 * cap);
-    L.ppar = o; o = align16(o + 4 * cap);
-    L.prho = o; o = align16(o + 4 * cap);
-    L.plrank = o; o = align16(o + 4 * cap);
-    L.ppop = o; o = align16(o + 4 * cap);
-    L.hist = o; o = align16(o + (cap > 0 ? 4 * kHistBins : 0));
+    // pool arrays: cap slots, kPoolPad zero keys, one store-sink slot per lane
+    const int pslots = cap > 0 ? cap + kPoolPad + kWave : 0;
+    L.pkey = o; o = align16(o + 8 * pslots);
+    L.ppar = o; o = align16(o + 4 * pslots);
+    L.prho = o; o = align16(o + 4 * pslots);
+    L.plrank = o; o = align16(o + 4 * pslots);
+    L.ppop = o; o = align16(o + 4 * pslots);
+    L.hist = o; o = align16(o + (cap > 0 ? 4 * (kHistBins + kWave) : 0));
     L.plvl = o; o = align16(o + (cap > 0 ? 4 * kLvlFloats : 0));
-    L.q0col = o; o = align16(o + 4 * kMaxB);
+    L.q0col = o; o = align16(o + 3 * 4 * kColLen);   // FamilyCols q0, q1n, t0
+    // FamilyWork: cmask, gpre, wtot, flag
+    L.fwork = o; o = align16(o + 8 * kFamGroups + 4 * kFamGroups + 4 * kFamRounds * (kThreads / kWave) + 16);
     L.total = o;
     return L;
 }
@@ -603,28 +608,54 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
     const int64_t tk0 = int64_t(q) * bk;
     const int kp = qrow_stride(k);
     S.kp = kp;
-    float *q0col = reinterpret_cast<float *>(smem + TL.q0col);
+    constexpr int kPoolCap = pool_cap(G);
+    // per-depth columns for the family walks (FamilyCols)
+    float *fq0 = reinterpret_cast<float *>(smem + TL.q0col);
+    float *fq1n = fq0 + kColLen;
+    int32_t *ft0 = reinterpret_cast<int32_t *>(fq1n + kColLen);
+    // the row status loads go out with the table loads: one round trip
+    const int32_t rst = tid < b ? ld_agent(P.row_status + int64_t(q) * b + tid) : int32_t(BASTION_Q_OK);
     for (int e = tid; e < b * kp; e += kThreads) {
         const int d = e / kp, j = e - d * kp;
         const float qv = j < k ? ld_agent(P.topk_q + tk0 + d * k + j) : 0.0f;
+        const int32_t tv = j < k ? ld_agent(P.topk_ids + tk0 + d * k + j) : 0;
         S.qtab[e] = qv;
-        S.ttab[e] = j < k ? ld_agent(P.topk_ids + tk0 + d * k + j) : 0;
-        if (j == 0) q0col[d] = qv;
+        S.ttab[e] = tv;
+        if (j == 0) {
+            fq0[d] = qv;
+            ft0[d] = tv;
+        }
+        if (j == 1 && d >= 1) fq1n[d - 1] = qv;
     }
-    for (int d = b + tid; d < kMaxB; d += kThreads) q0col[d] = 0.0f;
+    for (int d = tid; d < kColLen; d += kThreads) {
+        if (d >= b) {
+            fq0[d] = 0.0f;
+            ft0[d] = 0;
+        }
+        if (d >= b - 1 || k < 2) fq1n[d] = 0.0f;
+    }
+    FamilyWork FW;
+    FW.cmask = reinterpret_cast<uint64_t *>(smem + TL.fwork);
+    FW.gpre = reinterpret_cast<int32_t *>(FW.cmask + kFamGroups);
+    FW.wtot = FW.gpre + kFamGroups;
+    FW.flag = FW.wtot + kFamRounds * (kThreads / kWave);
+    if (kPoolCap > 0) {
+        uint32_t *hist = reinterpret_cast<uint32_t *>(smem + TL.hist);
+        int32_t *pop = reinterpret_cast<int32_t *>(smem + TL.ppop);
+        for (int i = tid; i < kHistBins + kWave; i += kThreads) hist[i] = 0u;
+        for (int i = tid; i < kPoolCap + kPoolPad + kWave; i += kThreads) pop[i] = 0;
+        if (tid == 0) FW.flag[0] = 0;
+    }
     const bool online = P.cost != nullptr;
     if (online)
         for (int e = tid; e <= nmax; e += kThreads)
             S.cost[e] = P.cost[int64_t(q) * P.cost_qstride + e];
     if (tid == 0) s_bad = 0;
     __syncthreads();
-    if (tid < b && ld_agent(P.row_status + int64_t(q) * b + tid) != BASTION_Q_OK)
-        atomicOr(&s_bad, 1);
+    if (rst != BASTION_Q_OK) atomicOr(&s_bad, 1);
     __syncthreads();
     const bool bad = s_bad != 0;
 
-    constexpr int kPoolCap = pool_cap(G);
-    __shared__ float s_bound;
     __shared__ int s_pool;
     int cnt = -1;
     if (kPoolCap > 0 && !bad) {
@@ -635,16 +666,41 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
         PL.lrank = reinterpret_cast<int32_t *>(smem + TL.plrank);
         PL.pop = reinterpret_cast<int32_t *>(smem + TL.ppop);
         PL.hist = reinterpret_cast<uint32_t *>(smem + TL.hist);
-        const float bound = family_bound<kThreads>(S.qtab, q0col, b, k, kp, nmax, PL.hist,
-                                                   reinterpret_cast<float *>(smem + TL.plvl),
-                                                   &s_bound);
-        if (wv == 0) {
-            const int n = pool_enumerate(PL, S.qtab, S.ttab, b, k, kp, bound, kPoolCap);
-            if (lane == 0) s_pool = n;
+        float *lvl = reinterpret_cast<float *>(smem + TL.plvl);
+        FamilyCols F;
+        F.q0 = fq0;
+        F.q1n = fq1n;
+        F.t0 = ft0;
+        const float bound = family_bound<kThreads>(S.qtab, S.ttab, F, b, k, kp, nmax, PL.hist, lvl);
+        // the family usually holds every node at or above the bound; if not,
+        // one wave enumerates them level by level
+        const int nf = family_select<kThreads>(PL, S.qtab, S.ttab, F, FW, b, k, kp, bound,
+                                               kPoolCap, lvl);
+        if (nf >= 1 && nf <= kPoolCap) {
+            FamGeom FG;
+            int tot;
+            FG.D = family_depth(b, k, tot);
+            int kD = 1;
+            for (int x = 0; x < FG.D; ++x) kD *= k;
+            FG.k = k;
+            FG.kp = kp;
+            FG.firstD = tot - kD;
+            FG.topbase = FW.flag[3];
+            FG.inv_k = (65536u + uint32_t(k) - 1u) / uint32_t(k);
+            FG.lvl = lvl;
+            FG.ttab = S.ttab;
+            FG.cmask = FW.cmask;
+            FG.gpre = FW.gpre;
+            cnt = family_rank<kThreads>(PL, FG, nf, nmax, kPoolCap, S.par, S.dep, S.tok, S.rho);
+        } else if (nf == -1) {
+            if (wv == 0) {
+                const int n = pool_enumerate(PL, S.qtab, S.ttab, b, k, kp, bound, kPoolCap);
+                if (lane == 0) s_pool = n;
+            }
+            __syncthreads();
+            const int n = s_pool;
+            if (n >= 1) cnt = pool_rank<kThreads>(PL, n, nmax, S.par, S.dep, S.tok, S.rho);
         }
-        __syncthreads();
-        const int n = s_pool;
-        if (n >= 1) cnt = pool_rank<kThreads>(PL, n, nmax, S.par, S.dep, S.tok, S.rho);
         __syncthreads();
     }
 

@@ -57,12 +57,6 @@ struct PoolLds {
 };
 
 
-__device__ __forceinline__ void hist_add(uint32_t *hist, float rho) {
-    uint32_t bin = __float_as_uint(rho) >> 20;
-    bin = bin < kHistBins ? bin : kHistBins - 1;
-    atomicAdd(hist + bin, 1u);
-}
-
 // inclusive prefix sum over the 64 lanes: DPP row shifts (zero fill) inside
 // each 16-lane row, then the totals of the rows below
 __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
@@ -75,104 +69,6 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
     const uint32_t r2 = uint32_t(__builtin_amdgcn_readlane(int(v), 47));
     const int row = lane_id() >> 4;
     return v + (row > 0 ? r0 : 0u) + (row > 1 ? r1 : 0u) + (row > 2 ? r2 : 0u);
-}
-
-// Step 1, by the whole block.  qtab[(d-1)*kp + j] is q of rank j at depth d
-// (rows padded with zeros to kp, a multiple of 8); q0col[d-1] is q of rank 0
-// at depth d (kMaxB entries, zero past b).  lvl holds kFamilyLevels floats
-// of scratch.  Returns (block-uniform) the lower bound t,
-// 0 when the family holds fewer than n nodes.
-template <int THREADS>
-__device__ __forceinline__ float family_bound(const float *qtab, const float *q0col, int b, int k,
-                                              int kp, int n, uint32_t *hist, float *lvl,
-                                              float *s_out) {
-    const int tid = threadIdx.x;
-    for (int i = tid; i < kHistBins; i += THREADS) hist[i] = 0u;
-    // complete levels 1..D (D as large as fits kFamilyLevels nodes)
-    int D = 0, tot = 0, szD = 1;
-    while (D < b && tot + szD * k <= kFamilyLevels) {
-        szD *= k;
-        tot += szD;
-        ++D;
-    }
-    // parent index i / k of node i of a level (i < 1024, k <= 32:
-    // (i * ceil(65536 / k)) >> 16 is exact)
-    const uint32_t inv_k = (65536u + uint32_t(k) - 1u) / uint32_t(k);
-    int off = 0, prev = 0, sz = 1;
-    for (int d = 1; d <= D; ++d) {
-        sz *= k;
-        __syncthreads();   // level d-1 (and the zeroed histogram) complete
-        for (int i = tid; i < sz; i += THREADS) {
-            const int p = int((uint32_t(i) * inv_k) >> 16), j = i - p * k;
-            const float rp = d == 1 ? 1.0f : lvl[prev + p];
-            const float v = __fmul_rn(rp, qtab[(d - 1) * kp + j]);
-            lvl[off + i] = v;
-            hist_add(hist, v);
-        }
-        prev = off;
-        off += sz;
-    }
-    // deeper than D: the top-1 path (pair index npair) and the paths leaving
-    // it once, at depth e with rank j >= 1, then following rank 0.  Each
-    // thread forms its path's rho from depth 1 in registers.
-    if (D < b) {
-        const int npair = b * (k - 1);
-        float q0[kMaxB];
-#pragma unroll
-        for (int d = 0; d < kMaxB; ++d) q0[d] = q0col[d];
-        for (int pi = tid; pi <= npair; pi += THREADS) {
-            const int e = pi < npair ? pi / (k - 1) + 1 : b + 1;
-            const int j = pi < npair ? pi - (e - 1) * (k - 1) + 1 : 0;
-            const float qe = qtab[(e <= b ? e - 1 : 0) * kp + j];
-            float r = 1.0f;
-#pragma unroll
-            for (int d = 1; d <= kMaxB; ++d) {
-                if (d <= b) {
-                    r = __fmul_rn(r, d == e ? qe : q0[d - 1]);
-                    if (d > D && d >= (e <= b ? e : 1)) hist_add(hist, r);
-                }
-            }
-        }
-    }
-    __syncthreads();
-    if (tid < kWave) {
-        // lane l owns bins 1008-16l .. 1023-16l; c[15] is its highest
-        const int lane = tid;
-        const pool_u32x4 *h4 =
-            reinterpret_cast<const pool_u32x4 *>(hist + (kHistBins - 16 - 16 * lane));
-        uint32_t c[16], own = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const pool_u32x4 v = h4[i];
-            c[4 * i + 0] = v[0];
-            c[4 * i + 1] = v[1];
-            c[4 * i + 2] = v[2];
-            c[4 * i + 3] = v[3];
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) own += c[i];
-        const uint32_t incl = wave_incl_scan_u32(own);
-        const uint64_t reach = __ballot(incl >= uint32_t(n));
-        if (reach) {
-            const int l = __ffsll((unsigned long long)reach) - 1;
-            if (lane == l) {
-                uint32_t acc = incl - own;
-                int bin = kHistBins - 16 - 16 * lane;
-                for (int i = 15; i >= 0; --i) {
-                    acc += c[i];
-                    if (acc >= uint32_t(n)) {
-                        bin = kHistBins - 16 - 16 * lane + i;
-                        break;
-                    }
-                }
-                *s_out = __uint_as_float(uint32_t(bin) << 20);
-            }
-        } else if (lane == 0) {
-            *s_out = 0.0f;
-        }
-    }
-    __syncthreads();
-    return *s_out;
 }
 
 // number of keys[f0..f1) greater than x; eight loads in flight at a time

@@ -153,6 +153,56 @@ def test_near_flat_rows_fill_the_pool():
     gc.run_and_check(x, 6, 120)
 
 
+def _deviations(g, q):
+    """per tree node of query q: depth and number of positions on its path
+    whose token is not that position's top-1 token"""
+    par, tok, dep = (gc.np_(g[f])[q] for f in ("parent", "token", "depth"))
+    top = gc.np_(g["topk_ids"])[q, :, 0]
+    out = []
+    for i in range(1, int(gc.np_(g["n_nodes"])[q]) + 1):
+        n, j = 0, i
+        while j > 0:
+            n += int(tok[j] != top[dep[j] - 1])
+            j = par[j]
+        out.append((int(dep[i]), n))
+    return out
+
+
+def test_two_uncertain_positions_leave_the_family():
+    """Two positions split evenly between two tokens, one inside the complete
+    top levels (k = 4: depths 1-4) and one below them: the tree holds nodes
+    that leave the top-1 path at both, which the family of one-deviation paths
+    does not contain, so the pool comes from the level-by-level enumeration."""
+    B, b, V = 2, 8, 512
+    x = torch.full((B, b, V), -4.0)
+    for p in range(b):
+        x[:, p, 10 + p] = 8.0
+    x[:, 1, 200] = 8.0
+    x[:, 5, 300] = 8.0
+    g, _ = gc.run_and_check(x.to("cuda"), 4, 32)
+    assert any(d > 4 and n >= 2 for d, n in _deviations(g, 0))
+
+
+def test_three_way_ties_below_the_top():
+    """Three equal logits under a clear top token at two positions: the
+    one-deviation paths through them tie at every later depth (same rho and
+    token), and best-first orders them by the tokens where they split."""
+    B, b, V = 3, 12, 1024
+    torch.manual_seed(8)
+    x = torch.randn((B, b, V)) * 0.3
+    for p in range(b):
+        x[:, p, 5 * p + 1] = 9.0
+    for p in (3, 7):
+        x[:, p, [700, 40, 333]] = 7.0
+    g, _ = gc.run_and_check(x.to(torch.bfloat16).to("cuda"), 8, 64)
+    par, rho, dep, tok = (gc.np_(g[f])[0] for f in ("parent", "rho", "depth", "token"))
+    # the tree does contain nodes of equal (rho, depth, token) under different parents
+    keys = {}
+    for i in range(1, int(gc.np_(g["n_nodes"])[0]) + 1):
+        keys.setdefault((float(rho[i]), int(dep[i]), int(tok[i])), set()).add(int(par[i]))
+    assert max(len(v) for v in keys.values()) >= 3
+
+
 def test_row_stride_padding_and_pos_base():
     wl = synth.scaled(synth.WORKLOADS["main"], B=2, b=4, V=1000, nmax=20)
     base = synth.make_logits(wl)
