@@ -78,6 +78,9 @@ struct Streamer {
     int k;
     float thv;     // float form of the wave threshold (-inf: none yet)
     uint64_t thk;  // the wave's current k-th best key (0: fewer than k so far)
+    uint64_t *bth; // the block's best such key (LDS): any wave's k-th best key
+                   // bounds the segment's k-th best from below, so every wave
+                   // filters with the largest one published
     int cnt;       // keys in ws->cand
     int nstage;
     int head;      // elements of the row before its first 16-byte aligned vector
@@ -86,8 +89,11 @@ struct Streamer {
     __device__ void compact() {
         uint64_t kth;
         cnt = wave_select_topk<kCap / kWave>(ws->cand, cnt, k, kth);
-        thk = kth;
-        thv = kth ? topk_key_value(kth) : -INFINITY;
+        if (kth > thk) {
+            thk = kth;
+            thv = topk_key_value(kth);
+            if (lane_id() == 0) atomicMax(reinterpret_cast<unsigned long long *>(bth), kth);
+        }
     }
 
     // Append the keys of the staged vectors that beat the threshold.
@@ -136,6 +142,7 @@ struct Streamer {
     __device__ __forceinline__ void tile(const u32x4 *raw, int vbase, const bool *valid,
                                          LaneSoftmax &sm) {
         constexpr int E = Elem<T>::kPerVec;
+        const uint64_t bk = *bth;   // read early: its latency hides under the tile's work
         float f[U][E];
         float vmax[U];
 #pragma unroll
@@ -182,7 +189,12 @@ struct Streamer {
             if (thk == 0 && t0 > thv) {
                 thv = t0;
                 thk = uint64_t(ord_f32(t0)) << 32;   // below every key of value t0
+                if (lane_id() == 0) atomicMax(reinterpret_cast<unsigned long long *>(bth), thk);
             }
+        }
+        if (bk > thk) {
+            thk = bk;
+            thv = topk_key_value(bk);
         }
         bool pass[U];
         bool any = false;
@@ -246,7 +258,11 @@ __device__ SegmentResult stream_segment(const BuildParams &P, const char *row, i
     const int v_lo = seg * per + (seg < rem ? seg : rem);
     const int v_hi = v_lo + per + (seg < rem ? 1 : 0);
 
+    __shared__ uint64_t s_bth;
+    if (tid == 0) s_bth = 0;
+    __syncthreads();
     Streamer<T, U> st;
+    st.bth = &s_bth;
     st.ws = &scr[wv];
     st.k = P.k;
     st.thv = -INFINITY;
@@ -671,10 +687,11 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
         F.q0 = fq0;
         F.q1n = fq1n;
         F.t0 = ft0;
-        const float bound = family_bound<kThreads>(S.qtab, S.ttab, F, b, k, kp, nmax, PL.hist, lvl);
+        FamRegs FR;
+        const float bound = family_bound<kThreads>(S.qtab, S.ttab, F, b, k, kp, nmax, PL.hist, lvl, FR);
         // the family usually holds every node at or above the bound; if not,
         // one wave enumerates them level by level
-        const int nf = family_select<kThreads>(PL, S.qtab, S.ttab, F, FW, b, k, kp, bound,
+        const int nf = family_select<kThreads>(PL, S.qtab, S.ttab, F, FW, FR, b, k, kp, bound,
                                                kPoolCap, lvl);
         if (nf >= 1 && nf <= kPoolCap) {
             FamGeom FG;

@@ -117,6 +117,15 @@ __device__ __forceinline__ Chain make_chain(int pi, int npair, int b, int k, int
     return c;
 }
 
+// What family_bound's path walk leaves in registers for family_select when
+// one thread holds one path (b * (k - 1) < THREADS): the path's rho at every
+// depth, rho one depth above its first family node, and the largest rho of a
+// child off the path (rank 1 one depth down) below a family node.
+struct FamRegs {
+    float rv[kMaxB];
+    float rp, escm;
+};
+
 // Step 1, by the whole block.  hist (kHistBins + kWave bins) must be zero
 // and visible to the block.  Writes the complete levels' rho to lvl[0, tot).
 // Returns the lower bound t (every wave reads the histogram itself), 0 when
@@ -124,7 +133,7 @@ __device__ __forceinline__ Chain make_chain(int pi, int npair, int b, int k, int
 template <int THREADS>
 __device__ __forceinline__ float family_bound(const float *qtab, const int32_t *ttab,
                                               const FamilyCols &F, int b, int k, int kp, int n,
-                                              uint32_t *hist, float *lvl) {
+                                              uint32_t *hist, float *lvl, FamRegs &R) {
     constexpr int W = THREADS / kWave;
     const int tid = threadIdx.x, lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -156,7 +165,36 @@ __device__ __forceinline__ float family_bound(const float *qtab, const int32_t *
     if (D < b) {
         const int npair = b * (k - 1);
         const uint32_t inv_km1 = (65536u + uint32_t(k - 1) - 1u) / uint32_t(k - 1);
-        for (int p0 = 0; p0 <= npair; p0 += THREADS) {
+        if (npair < THREADS) {
+            // one path per thread, kept in registers for family_select
+            const Chain c = make_chain(tid, npair, b, k, kp, D, inv_km1, qtab, ttab);
+            const int lo = c.valid ? c.dstart : kMaxB + 1;
+            float r = 1.0f, rp = 1.0f, em = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kMaxB; ++i) R.rv[i] = 0.0f;   // depths past b: below any t > 0
+#pragma unroll
+            for (int g4 = 0; g4 < kMaxB / 4; ++g4) {
+                const int d0 = 1 + 4 * g4;
+                if (d0 <= b) {
+                    const pool_f32x4 q4 = *reinterpret_cast<const pool_f32x4 *>(F.q0 + d0 - 1);
+                    const pool_f32x4 n4 = *reinterpret_cast<const pool_f32x4 *>(F.q1n + d0 - 1);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int d = d0 + u;
+                        if (d <= b) {
+                            rp = d == c.dstart ? r : rp;
+                            r = __fmul_rn(r, d == c.e ? c.qe : q4[u]);
+                            R.rv[4 * g4 + u] = r;
+                            em = d >= lo ? fmaxf(em, __fmul_rn(r, n4[u])) : em;
+                            if (d > D) atomicAdd(hist + (d >= lo ? hist_bin(r) : kHistBins + lane), 1u);
+                        }
+                    }
+                }
+            }
+            R.rp = rp;
+            R.escm = em;
+        }
+        for (int p0 = 0; npair >= THREADS && p0 <= npair; p0 += THREADS) {
             const Chain c = make_chain(p0 + tid, npair, b, k, kp, D, inv_km1, qtab, ttab);
             const int lo = c.valid ? c.dstart : kMaxB + 1;
             float r = 1.0f;
@@ -216,8 +254,8 @@ __device__ __forceinline__ float family_bound(const float *qtab, const int32_t *
 // slots n .. n + kPoolPad - 1 get zero keys.  Ends with a barrier.
 template <int THREADS>
 __device__ int family_select(const PoolLds &L, const float *qtab, const int32_t *ttab,
-                             const FamilyCols &F, const FamilyWork &Wk, int b, int k, int kp,
-                             float t, int cap, const float *lvl) {
+                             const FamilyCols &F, const FamilyWork &Wk, const FamRegs &R, int b,
+                             int k, int kp, float t, int cap, const float *lvl) {
     constexpr int W = THREADS / kWave, MC = kFamilyLevels / THREADS;
     static_assert(kFamilyLevels % THREADS == 0 && MC * W == kFamGroups, "family groups");
     const int tid = threadIdx.x, lane = lane_id();
@@ -278,26 +316,44 @@ __device__ int family_select(const PoolLds &L, const float *qtab, const int32_t 
             // deepest qualifying depth (last), the deepest node whose rank-1
             // child qualifies (escd; q1n is zero past the last depth and
             // t > 0), rho at dstart - 1 (rp)
-            float r = 1.0f, rp = 1.0f;
-            int last = 0, escd = 0;
-            auto step = [&](int d, float q, float qn) {
-                rp = d == c.dstart ? r : rp;
-                r = __fmul_rn(r, d == c.e ? c.qe : q);
-                last = r >= t ? d : last;
-                escd = __fmul_rn(r, qn) >= t ? d : escd;
-            };
-            for (int d0 = 1; d0 <= bfull; d0 += 4) {
-                const pool_f32x4 q4 = *reinterpret_cast<const pool_f32x4 *>(F.q0 + d0 - 1);
-                const pool_f32x4 n4 = *reinterpret_cast<const pool_f32x4 *>(F.q1n + d0 - 1);
+            float rp = 1.0f;
+            int last = 0;
+            bool escp = false;
+            if (rounds == 1) {
+                // the path's values from family_bound's walk (zero past b,
+                // and t > 0 here); rho never grows along the path
+                if (b <= 16) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) step(d0 + u, q4[u], n4[u]);
+                    for (int i = 0; i < 16; ++i) last += R.rv[i] >= t ? 1 : 0;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < kMaxB; ++i) last += R.rv[i] >= t ? 1 : 0;
+                }
+                rp = R.rp;
+                escp = R.escm >= t;
+            } else {
+                float r = 1.0f;
+                int escd = 0;
+                auto step = [&](int d, float q, float qn) {
+                    rp = d == c.dstart ? r : rp;
+                    r = __fmul_rn(r, d == c.e ? c.qe : q);
+                    last = r >= t ? d : last;
+                    escd = __fmul_rn(r, qn) >= t ? d : escd;
+                };
+                for (int d0 = 1; d0 <= bfull; d0 += 4) {
+                    const pool_f32x4 q4 = *reinterpret_cast<const pool_f32x4 *>(F.q0 + d0 - 1);
+                    const pool_f32x4 n4 = *reinterpret_cast<const pool_f32x4 *>(F.q1n + d0 - 1);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) step(d0 + u, q4[u], n4[u]);
+                }
+                for (int d = bfull + 1; d <= b; ++d) step(d, F.q0[d - 1], F.q1n[d - 1]);
+                escp = escd >= c.dstart;
             }
-            for (int d = bfull + 1; d <= b; ++d) step(d, F.q0[d - 1], F.q1n[d - 1]);
             // the top-1 path's children off it are one-deviation paths
             const bool dev = c.valid && !c.top;
             cn[rd] = (c.valid && last >= c.dstart) ? last - c.dstart + 1 : 0;
             crp[rd] = rp;
-            esc = esc || (dev && escd >= c.dstart);
+            esc = esc || (dev && escp);
             const uint32_t incl = wave_incl_scan_u32(uint32_t(cn[rd]));
             cbase[rd] = int(incl) - cn[rd];
             if (lane == kWave - 1) Wk.wtot[rd * W + wv] = int(incl);
