@@ -768,14 +768,22 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
     const int K = P.K, b = P.b, k = P.k, C = K * k, nmax = P.nmax;
     const MixLds M = mix_lds(smem, mix_layout(K, b, k, nmax));
     const int64_t r0 = int64_t(q) * K * b;
-    __shared__ int s_bad, s_cnt, s_ns, s_np;
+    __shared__ int s_bad, s_ns, s_np;
     __shared__ uint64_t s_tau;
     if (tid == 0) s_bad = 0;
+    for (int i = tid; i < b; i += kThreads) M.cnt[i] = 0;
     __syncthreads();
+    // one round trip: row statistics, row status and every position's top-k
+    // ids (ids[pos * C + z * k + j] = candidate j of branch z)
     for (int e = tid; e < K * b; e += kThreads) {
         M.rowm[e] = ld_agent(P.row_ms + 2 * (r0 + e));
         M.rows[e] = ld_agent(P.row_ms + 2 * (r0 + e) + 1);
         if (ld_agent(P.row_status + r0 + e) != BASTION_Q_OK) atomicOr(&s_bad, 1);
+    }
+    for (int e = tid; e < b * C; e += kThreads) {
+        const int pos = e / C, c = e - pos * C;
+        const int z = c / k, j = c - z * k;
+        M.ids[e] = ld_agent(P.topk_ids + (r0 + z * b + pos) * k + j);
     }
     if (tid == 0) {
         // prior weights, float64 softmax
@@ -801,23 +809,91 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         if (P.mix_tree) emit_tree(P, q, M.par, M.dep, M.tok, M.rho, M.ahat, 0, true, BASTION_Q_BAD_LOGITS);
         return;
     }
-    // chains: the top-1 token of every branch row
+    // chains: the top-1 token of every branch row (chain[z * b + i])
     for (int e = tid; e < K * b; e += kThreads) {
-        const int t = ld_agent(P.topk_ids + (r0 + e) * k);
+        const int z = e / b, i = e - z * b;
+        const int t = M.ids[i * C + z * k];
         M.chain[e] = t;
         P.chain_tokens[r0 + e] = t;
     }
+    // unions, every position at once: first occurrences ...
+    for (int e = tid; e < b * C; e += kThreads) {
+        const int pos = e / C, c = e - pos * C;
+        const int32_t *ids = M.ids + pos * C;
+        const int t = ids[c];
+        int f = 1;
+        for (int c2 = 0; c2 < c; ++c2) f = (ids[c2] == t) ? 0 : f;
+        M.first[e] = f;
+    }
+    __syncthreads();
+    // ... then their ascending ranks
+    for (int e = tid; e < b * C; e += kThreads) {
+        const int pos = e / C, c = e - pos * C;
+        if (M.first[e]) {
+            const int32_t *ids = M.ids + pos * C;
+            const int32_t *fst = M.first + pos * C;
+            const int t = ids[c];
+            int r = 0;
+            for (int c2 = 0; c2 < C; ++c2) r += (fst[c2] && ids[c2] < t) ? 1 : 0;
+            M.ctok[pos * C + r] = t;
+            atomicAdd(M.cnt + pos, 1);
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < b * C; e += kThreads) {
+        const int pos = e / C, c = e - pos * C;
+        P.cand_tokens[cbase + e] = c < M.cnt[pos] ? M.ctok[e] : -1;
+    }
+    for (int i = tid; i < b; i += kThreads) P.cand_count[int64_t(q) * b + i] = M.cnt[i];
+    // every logit the stage needs, in batches of independent loads:
+    //   chain entries  x < K*K*b: (z, z', i) -> q_i(chain z | z') into qc;
+    //   candidate entries: (pos, c, z) -> q_pos(ctok | z) into cand_q
+    // (the row's own top-k formula: exp2(l log2e - C) / S)
+    {
+        constexpr int NB = 16;
+        const int nch = K * K * b, tot = nch + b * C * K;
+        for (int x0 = 0; x0 < tot; x0 += NB * kThreads) {
+            float lv[NB];
+            int lr[NB];
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const int x = x0 + u * kThreads + tid;
+                lv[u] = 0.0f;
+                lr[u] = -1;
+                if (x < nch) {
+                    const int zz = x / b, i = x - zz * b;
+                    const int z = zz / K, zp = zz - z * K;
+                    lr[u] = zp * b + i;
+                    lv[u] = mix_logit(P, r0 + lr[u], M.chain[z * b + i], P.is_bf16);
+                } else if (x < tot) {
+                    const int y = x - nch;
+                    const int pc = y / K, z = y - pc * K;
+                    const int pos = pc / C, c = pc - pos * C;
+                    if (c < M.cnt[pos]) {
+                        lr[u] = z * b + pos;
+                        lv[u] = mix_logit(P, r0 + lr[u], M.ctok[pos * C + c], P.is_bf16);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const int x = x0 + u * kThreads + tid;
+                const float v = lr[u] >= 0
+                    ? __builtin_amdgcn_exp2f(__builtin_fmaf(lv[u], kLog2e, -scale_ref(M.rowm[lr[u]]))) /
+                          M.rows[lr[u]]
+                    : 0.0f;
+                if (x < nch) M.qc[x] = v;
+                else if (x < tot) P.cand_q[cbase * K + (x - nch)] = v;
+            }
+        }
+    }
+    // the cand_q stores are read back by this block below
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     // q_dep: thread (z, z') forms prod_i q_i(chain z | z') in float64
     for (int t = tid; t < K * K; t += kThreads) {
-        const int z = t / K, zp = t - z * K;
         double pr = 1.0;
-        for (int i = 0; i < b; ++i) {
-            const int lr = zp * b + i;
-            const float l = mix_logit(P, r0 + lr, M.chain[z * b + i], P.is_bf16);
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(l, kLog2e, -scale_ref(M.rowm[lr])));
-            pr *= double(e / M.rows[lr]);
-        }
+        for (int i = 0; i < b; ++i) pr *= double(M.qc[t * b + i]);
         M.prod[t] = pr;
     }
     __syncthreads();
@@ -826,54 +902,29 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         for (int zp = 0; zp < K; ++zp) qd += M.w[zp] * M.prod[z * K + zp];
         P.qdep[q * K + z] = qd;
     }
-    // candidates and the tree, position by position
+    if (!P.mix_tree) return;
+    // the tree, round by round; a round's q table (C x K) comes from cand_q,
+    // prefetched one round ahead into the other LDS buffer
+    const int nq = C * K;
+    const float *cqg = P.cand_q + cbase * K;
+    for (int e = tid; e < nq; e += kThreads) M.cq[e] = ld_agent(cqg + e);
+    __syncthreads();
     int nR = 0;
-    bool grow = P.mix_tree != 0;
     for (int d = 1; d <= b; ++d) {
         const int pos = d - 1;
-        if (tid == 0) s_cnt = 0;
-        for (int c = tid; c < C; c += kThreads) {
-            const int z = c / k, j = c - z * k;
-            M.ids[c] = ld_agent(P.topk_ids + (r0 + z * b + pos) * k + j);
+        MixLds Mr = M;
+        Mr.cq = (pos & 1) ? M.cq2 : M.cq;
+        Mr.ctok = M.ctok + pos * C;
+        float *nxt = (pos & 1) ? M.cq : M.cq2;
+        // next round's table: loads now, LDS stores at the end of the round
+        constexpr int NQ = 8;   // entries per thread held in registers
+        float pre[NQ];
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) {
+            const int e = u * kThreads + tid;
+            pre[u] = (d < b && e < nq) ? ld_agent(cqg + int64_t(d) * nq + e) : 0.0f;
         }
-        __syncthreads();
-        // first occurrences, then their ascending ranks
-        for (int c = tid; c < C; c += kThreads) {
-            const int t = M.ids[c];
-            int f = 1;
-            for (int c2 = 0; c2 < c; ++c2) f = (M.ids[c2] == t) ? 0 : f;
-            M.first[c] = f;
-        }
-        __syncthreads();
-        for (int c = tid; c < C; c += kThreads) {
-            if (M.first[c]) {
-                const int t = M.ids[c];
-                int r = 0;
-                for (int c2 = 0; c2 < C; ++c2) r += (M.first[c2] && M.ids[c2] < t) ? 1 : 0;
-                M.ctok[r] = t;
-                atomicAdd(&s_cnt, 1);
-            }
-        }
-        __syncthreads();
-        const int cnt = s_cnt;
-        int32_t *ct_out = P.cand_tokens + cbase + int64_t(pos) * C;
-        for (int c = tid; c < C; c += kThreads) ct_out[c] = c < cnt ? M.ctok[c] : -1;
-        if (tid == 0) P.cand_count[int64_t(q) * b + pos] = cnt;
-        // q of every candidate in every branch (the row's own top-k formula)
-        float *cq_out = P.cand_q + (cbase + int64_t(pos) * C) * K;
-        for (int e = tid; e < C * K; e += kThreads) {
-            const int c = e / K, z = e - c * K;
-            float v = 0.0f;
-            if (c < cnt) {
-                const int lr = z * b + pos;
-                const float l = mix_logit(P, r0 + lr, M.ctok[c], P.is_bf16);
-                v = __builtin_amdgcn_exp2f(__builtin_fmaf(l, kLog2e, -scale_ref(M.rowm[lr]))) / M.rows[lr];
-                M.cq[e] = v;
-            }
-            cq_out[e] = v;
-        }
-        __syncthreads();
-        if (!grow) continue;
+        const int cnt = M.cnt[pos];
         // tree round d: the parents are the depth-(d-1) entries, in order
         if (d == 1) {
             if (tid < K) M.ptab[tid] = 1.0f;
@@ -899,17 +950,13 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         }
         __syncthreads();
         const int np = s_np;
-        if (np == 0) {
-            grow = false;
-            continue;
-        }
         const int total = np * cnt;
         for (int base = 0; base < total; base += kThreads) {
             const int idx = base + tid;
             if (idx < total) {
                 const int p = idx / cnt, c = idx - p * cnt;
-                const float score = mix_child(M, K, p, c);
-                const uint64_t key = tree_key(score, d, M.ctok[c], p);
+                const float score = mix_child(Mr, K, p, c);
+                const uint64_t key = tree_key(score, d, Mr.ctok[c], p);
                 if (key > s_tau) {
                     const int slot = atomicAdd(&s_ns, 1);
                     M.skey[slot] = key;
@@ -921,7 +968,7 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
             // merge when the buffer could not take another chunk, at the end
             // of the round, and while the list is not full (to set its N-th key)
             if (ns > 0 && (ns > kMixSurv - kThreads || base + kThreads >= total || nR < nmax)) {
-                nR = mix_merge<kThreads>(M, K, nmax, nR, ns);
+                nR = mix_merge<kThreads>(Mr, K, nmax, nR, ns);
                 if (tid == 0) {
                     s_ns = 0;
                     s_tau = nR == nmax ? M.rkey[nmax - 1] : 0;
@@ -929,8 +976,17 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
                 __syncthreads();
             }
         }
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) {
+            const int e = u * kThreads + tid;
+            if (d < b && e < nq) nxt[e] = pre[u];
+        }
+        // tables larger than the prefetch (K * k > 64 with many branches)
+        for (int e = NQ * kThreads + tid; d < b && e < nq; e += kThreads)
+            nxt[e] = ld_agent(cqg + int64_t(d) * nq + e);
+        __syncthreads();
+        if (np == 0) break;
     }
-    if (!P.mix_tree) return;
     if (wv == 0) {
         mix_resolve(M, b, nmax, nR);
         ahat_fill(M.rho, M.ahat, nR);
@@ -1041,6 +1097,10 @@ __global__ __launch_bounds__(kThreads, (R >= 16 ? 2 : 4)) void build_trees_kerne
         }
     }
     if (!arrive_last(P.query_ticket + q, uint32_t(P.rows_per_query))) return;
+    // The query stage is latency-bound and other queries' streams on this CU
+    // wait for its results no more than it waits for them: issue ahead of
+    // them (a finished stream leaves this block's waves at priority 0).
+    __builtin_amdgcn_s_setprio(3);
     if constexpr (MODE == 1) mixture_stage(P, q, smem);
     else tree_stage<R>(P, q, smem);
 }

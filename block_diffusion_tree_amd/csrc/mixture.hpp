@@ -9,7 +9,10 @@
 //      from the branch row's max and sum at the chain token (logit gather);
 //   3. per position, the union of the branches' top-k tokens in ascending
 //      order and q_i(token | z) for every branch (float32, the same formula
-//      as the row's own top-k q);
+//      as the row's own top-k q).  All positions are handled at once: one
+//      round trip loads every branch row's top-k ids, the unions are formed
+//      in LDS, and every logit the stage needs (chains and candidates) is
+//      gathered in a few batches of independent loads;
 //   4. when asked, the best-first tree over those candidates.  A node keeps
 //      r_z = fl32 product of q_i(x_i | z) along its path and is scored by the
 //      float32 fma chain sum_z w_z r_z; children score no higher than their
@@ -18,7 +21,9 @@
 //      round d merging the children of its depth-(d-1) nodes.  A child's key
 //      carries its parent's rank among the depth-(d-1) entries, which is
 //      best-first's parent-order tie-break.  Candidates that beat the list's
-//      N-th key are buffered and merged kMixSurv at a time.
+//      N-th key are buffered and merged kMixSurv at a time.  A round reads
+//      its position's q table from the cand_q output, prefetched into LDS
+//      one round ahead.
 #pragma once
 
 #include "device_common.hpp"
@@ -29,12 +34,15 @@ namespace bastion {
 constexpr int kMixSurv = 512;   // survivors buffered between merges
 
 struct MixLayout {
-    int w, wq, prod, rowm, rows, chain, ids, first, ctok, cq, rkey, rr, nkey, nr, ptab, skey, sinfo, map,
-        base, par, dep, tok, rho, ahat, total;
+    int w, wq, prod, rowm, rows, chain, ids, first, ctok, cnt, qc, cq, cq2, rkey, rr, nkey, nr, ptab, skey,
+        sinfo, map, base, par, dep, tok, rho, ahat, total;
 };
 
 __host__ __device__ inline int mix_align16(int x) { return (x + 15) & ~15; }
 
+// Three regions: arrays live through the whole stage; arrays used only
+// before the tree rounds (every position's ids, first-occurrence flags, the
+// chains' q); arrays used only by the rounds.  The last two share space.
 __host__ __device__ inline MixLayout mix_layout(int K, int b, int k, int nmax) {
     MixLayout L;
     const int C = K * k, nn = nmax + 2;
@@ -45,17 +53,8 @@ __host__ __device__ inline MixLayout mix_layout(int K, int b, int k, int nmax) {
     L.rowm = o;  o = mix_align16(o + 4 * K * b);
     L.rows = o;  o = mix_align16(o + 4 * K * b);
     L.chain = o; o = mix_align16(o + 4 * K * b);
-    L.ids = o;   o = mix_align16(o + 4 * C);
-    L.first = o; o = mix_align16(o + 4 * C);
-    L.ctok = o;  o = mix_align16(o + 4 * C);
-    L.cq = o;    o = mix_align16(o + 4 * C * K);
-    L.rkey = o;  o = mix_align16(o + 8 * nmax);
-    L.rr = o;    o = mix_align16(o + 4 * nmax * K);
-    L.nkey = o;  o = mix_align16(o + 8 * nmax);
-    L.nr = o;    o = mix_align16(o + 4 * nmax * K);
-    L.ptab = o;  o = mix_align16(o + 4 * nmax * K);
-    L.skey = o;  o = mix_align16(o + 8 * kMixSurv);
-    L.sinfo = o; o = mix_align16(o + 4 * kMixSurv);
+    L.ctok = o;  o = mix_align16(o + 4 * b * C);   // unions, ascending, per position
+    L.cnt = o;   o = mix_align16(o + 4 * b);
     L.map = o;   o = mix_align16(o + 4 * nn);
     L.base = o;  o = mix_align16(o + 4 * 40);
     L.par = o;   o = mix_align16(o + 4 * nn);
@@ -63,14 +62,31 @@ __host__ __device__ inline MixLayout mix_layout(int K, int b, int k, int nmax) {
     L.tok = o;   o = mix_align16(o + 4 * nn);
     L.rho = o;   o = mix_align16(o + 4 * nn);
     L.ahat = o;  o = mix_align16(o + 8 * nn);
-    L.total = o;
+    // before the rounds
+    int a = o;
+    L.ids = a;   a = mix_align16(a + 4 * b * C);   // every position's top-k ids
+    L.first = a; a = mix_align16(a + 4 * b * C);
+    L.qc = a;    a = mix_align16(a + 4 * K * K * b); // q_i(chain z | z')
+    // the rounds
+    int r = o;
+    L.cq = r;    r = mix_align16(r + 4 * C * K);   // one position's q table, two buffers
+    L.cq2 = r;   r = mix_align16(r + 4 * C * K);
+    L.rkey = r;  r = mix_align16(r + 8 * nmax);
+    L.rr = r;    r = mix_align16(r + 4 * nmax * K);
+    L.nkey = r;  r = mix_align16(r + 8 * nmax);
+    L.nr = r;    r = mix_align16(r + 4 * nmax * K);
+    L.ptab = r;  r = mix_align16(r + 4 * nmax * K);
+    L.skey = r;  r = mix_align16(r + 8 * kMixSurv);
+    L.sinfo = r; r = mix_align16(r + 4 * kMixSurv);
+    L.total = a > r ? a : r;
     return L;
 }
 
 struct MixLds {
     double *w, *prod;
     float *wq, *rowm, *rows, *cq, *rr, *nr, *ptab;
-    int32_t *chain, *ids, *first, *ctok, *sinfo, *map, *base, *par, *dep, *tok;
+    int32_t *chain, *ids, *first, *ctok, *cnt, *sinfo, *map, *base, *par, *dep, *tok;
+    float *qc, *cq2;
     uint64_t *rkey, *nkey, *skey;
     float *rho;
     double *ahat;
@@ -87,7 +103,10 @@ __device__ __forceinline__ MixLds mix_lds(char *smem, const MixLayout &L) {
     M.ids = reinterpret_cast<int32_t *>(smem + L.ids);
     M.first = reinterpret_cast<int32_t *>(smem + L.first);
     M.ctok = reinterpret_cast<int32_t *>(smem + L.ctok);
+    M.cnt = reinterpret_cast<int32_t *>(smem + L.cnt);
+    M.qc = reinterpret_cast<float *>(smem + L.qc);
     M.cq = reinterpret_cast<float *>(smem + L.cq);
+    M.cq2 = reinterpret_cast<float *>(smem + L.cq2);
     M.rkey = reinterpret_cast<uint64_t *>(smem + L.rkey);
     M.rr = reinterpret_cast<float *>(smem + L.rr);
     M.nkey = reinterpret_cast<uint64_t *>(smem + L.nkey);
