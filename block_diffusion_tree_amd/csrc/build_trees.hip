@@ -816,27 +816,42 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         M.chain[e] = t;
         P.chain_tokens[r0 + e] = t;
     }
-    // unions, every position at once: first occurrences ...
-    for (int e = tid; e < b * C; e += kThreads) {
-        const int pos = e / C, c = e - pos * C;
-        const int32_t *ids = M.ids + pos * C;
-        const int t = ids[c];
-        int f = 1;
-        for (int c2 = 0; c2 < c; ++c2) f = (ids[c2] == t) ? 0 : f;
-        M.first[e] = f;
-    }
-    __syncthreads();
-    // ... then their ascending ranks
-    for (int e = tid; e < b * C; e += kThreads) {
-        const int pos = e / C, c = e - pos * C;
-        if (M.first[e]) {
+    if (C <= kWave) {
+        // unions, one position per wave at a time: sort the C tokens across
+        // the lanes (ascending; padding lanes hold INT_MAX), keep the first of
+        // every run of equal tokens
+        for (int pos = wv; pos < b; pos += kThreads / kWave) {
+            int t = lane < C ? M.ids[pos * C + lane] : 0x7FFFFFFF;
+            t = int(sort64_asc_u32(uint32_t(t)));
+            const int prev = __shfl_up(t, 1);
+            const bool keep = lane < C && (lane == 0 || prev != t);
+            const uint64_t m = __ballot(keep);
+            if (keep) M.ctok[pos * C + popc64(m & lanemask_lt())] = t;
+            if (lane == 0) M.cnt[pos] = popc64(m);
+        }
+    } else {
+        // unions, every position at once: first occurrences ...
+        for (int e = tid; e < b * C; e += kThreads) {
+            const int pos = e / C, c = e - pos * C;
             const int32_t *ids = M.ids + pos * C;
-            const int32_t *fst = M.first + pos * C;
             const int t = ids[c];
-            int r = 0;
-            for (int c2 = 0; c2 < C; ++c2) r += (fst[c2] && ids[c2] < t) ? 1 : 0;
-            M.ctok[pos * C + r] = t;
-            atomicAdd(M.cnt + pos, 1);
+            int f = 1;
+            for (int c2 = 0; c2 < c; ++c2) f = (ids[c2] == t) ? 0 : f;
+            M.first[e] = f;
+        }
+        __syncthreads();
+        // ... then their ascending ranks
+        for (int e = tid; e < b * C; e += kThreads) {
+            const int pos = e / C, c = e - pos * C;
+            if (M.first[e]) {
+                const int32_t *ids = M.ids + pos * C;
+                const int32_t *fst = M.first + pos * C;
+                const int t = ids[c];
+                int r = 0;
+                for (int c2 = 0; c2 < C; ++c2) r += (fst[c2] && ids[c2] < t) ? 1 : 0;
+                M.ctok[pos * C + r] = t;
+                atomicAdd(M.cnt + pos, 1);
+            }
         }
     }
     __syncthreads();
@@ -857,23 +872,25 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
             int lr[NB];
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
+                // the entry's branch row and token, without branches; an
+                // entry past the end or past its position's union re-reads
+                // token 0 of the query's first row and is discarded
                 const int x = x0 + u * kThreads + tid;
-                lv[u] = 0.0f;
-                lr[u] = -1;
-                if (x < nch) {
-                    const int zz = x / b, i = x - zz * b;
-                    const int z = zz / K, zp = zz - z * K;
-                    lr[u] = zp * b + i;
-                    lv[u] = mix_logit(P, r0 + lr[u], M.chain[z * b + i], P.is_bf16);
-                } else if (x < tot) {
-                    const int y = x - nch;
-                    const int pc = y / K, z = y - pc * K;
-                    const int pos = pc / C, c = pc - pos * C;
-                    if (c < M.cnt[pos]) {
-                        lr[u] = z * b + pos;
-                        lv[u] = mix_logit(P, r0 + lr[u], M.ctok[pos * C + c], P.is_bf16);
-                    }
-                }
+                const bool ch = x < nch;
+                const int zz = x / b, i = x - zz * b;                 // chain entry
+                const int y = x - nch;
+                const int pc = y / K, zc = y - pc * K;                // candidate entry
+                const int pos = pc / C, c = pc - pos * C;
+                // (y < 0 for chain entries: clamp what it indexes)
+                const int posc = (y >= 0 && pos < b) ? pos : 0;
+                const int cc = (y >= 0 && c < C) ? c : 0;
+                const int zcc = y >= 0 ? zc : 0;
+                const bool cv = !ch && x < tot && cc < M.cnt[posc];
+                const int zch = ch ? zz : 0;
+                const int row = ch ? (zch - (zch / K) * K) * b + i : zcc * b + posc;
+                const int tok = ch ? M.chain[(zch / K) * b + i] : M.ctok[posc * C + cc];
+                lr[u] = (ch || cv) ? row : -1;
+                lv[u] = mix_logit(P, r0 + (lr[u] >= 0 ? row : 0), lr[u] >= 0 ? tok : 0, P.is_bf16);
             }
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
@@ -951,29 +968,56 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         __syncthreads();
         const int np = s_np;
         const int total = np * cnt;
-        for (int base = 0; base < total; base += kThreads) {
-            const int idx = base + tid;
-            if (idx < total) {
+        // one pass over all children without barriers: the survivors (keys
+        // above the running list's N-th) go to the buffer while it has room
+        {
+            const uint64_t tau = s_tau;
+            for (int idx = tid; idx < total; idx += kThreads) {
                 const int p = idx / cnt, c = idx - p * cnt;
                 const float score = mix_child(Mr, K, p, c);
                 const uint64_t key = tree_key(score, d, Mr.ctok[c], p);
-                if (key > s_tau) {
+                if (key > tau) {
                     const int slot = atomicAdd(&s_ns, 1);
-                    M.skey[slot] = key;
-                    M.sinfo[slot] = (p << 16) | c;
+                    if (slot < kMixSurv) {
+                        M.skey[slot] = key;
+                        M.sinfo[slot] = (p << 16) | c;
+                    }
                 }
             }
+        }
+        __syncthreads();
+        if (s_ns <= kMixSurv) {
+            if (s_ns > 0) nR = mix_merge<kThreads>(Mr, K, nmax, nR, s_ns);
+        } else {
+            // too many survivors (the list is still filling): chunk by chunk,
+            // merging as the buffer fills, which raises the N-th key
             __syncthreads();
-            const int ns = s_ns;
-            // merge when the buffer could not take another chunk, at the end
-            // of the round, and while the list is not full (to set its N-th key)
-            if (ns > 0 && (ns > kMixSurv - kThreads || base + kThreads >= total || nR < nmax)) {
-                nR = mix_merge<kThreads>(Mr, K, nmax, nR, ns);
-                if (tid == 0) {
-                    s_ns = 0;
-                    s_tau = nR == nmax ? M.rkey[nmax - 1] : 0;
+            if (tid == 0) s_ns = 0;
+            __syncthreads();
+            for (int base = 0; base < total; base += kThreads) {
+                const int idx = base + tid;
+                if (idx < total) {
+                    const int p = idx / cnt, c = idx - p * cnt;
+                    const float score = mix_child(Mr, K, p, c);
+                    const uint64_t key = tree_key(score, d, Mr.ctok[c], p);
+                    if (key > s_tau) {
+                        const int slot = atomicAdd(&s_ns, 1);
+                        M.skey[slot] = key;
+                        M.sinfo[slot] = (p << 16) | c;
+                    }
                 }
                 __syncthreads();
+                const int ns = s_ns;
+                // merge when the buffer could not take another chunk, at the
+                // end of the round, and while the list is not full
+                if (ns > 0 && (ns > kMixSurv - kThreads || base + kThreads >= total || nR < nmax)) {
+                    nR = mix_merge<kThreads>(Mr, K, nmax, nR, ns);
+                    if (tid == 0) {
+                        s_ns = 0;
+                        s_tau = nR == nmax ? M.rkey[nmax - 1] : 0;
+                    }
+                    __syncthreads();
+                }
             }
         }
 #pragma unroll

@@ -99,6 +99,40 @@ __device__ __forceinline__ void sort64_desc(uint32_t &h, uint32_t &l) {
     cmpx<1>(h, l, true);
 }
 
+// bitonic sort of one 32-bit value per lane into ascending lane order
+template <int S>
+__device__ __forceinline__ uint32_t cmpx_u32(uint32_t v, bool asc) {
+    const uint32_t o = xpartner<S>(v);
+    const bool lower = (lane_id() & S) == 0;
+    return (lower == asc) ? min(v, o) : max(v, o);
+}
+
+__device__ __forceinline__ uint32_t sort64_asc_u32(uint32_t v) {
+    const int lane = lane_id();
+    v = cmpx_u32<1>(v, (lane & 2) == 0);
+    v = cmpx_u32<2>(v, (lane & 4) == 0);
+    v = cmpx_u32<1>(v, (lane & 4) == 0);
+    v = cmpx_u32<4>(v, (lane & 8) == 0);
+    v = cmpx_u32<2>(v, (lane & 8) == 0);
+    v = cmpx_u32<1>(v, (lane & 8) == 0);
+    v = cmpx_u32<8>(v, (lane & 16) == 0);
+    v = cmpx_u32<4>(v, (lane & 16) == 0);
+    v = cmpx_u32<2>(v, (lane & 16) == 0);
+    v = cmpx_u32<1>(v, (lane & 16) == 0);
+    v = cmpx_u32<16>(v, (lane & 32) == 0);
+    v = cmpx_u32<8>(v, (lane & 32) == 0);
+    v = cmpx_u32<4>(v, (lane & 32) == 0);
+    v = cmpx_u32<2>(v, (lane & 32) == 0);
+    v = cmpx_u32<1>(v, (lane & 32) == 0);
+    v = cmpx_u32<32>(v, true);
+    v = cmpx_u32<16>(v, true);
+    v = cmpx_u32<8>(v, true);
+    v = cmpx_u32<4>(v, true);
+    v = cmpx_u32<2>(v, true);
+    v = cmpx_u32<1>(v, true);
+    return v;
+}
+
 // bitonic sequence in one register -> descending
 __device__ __forceinline__ void merge64_desc(uint32_t &h, uint32_t &l) {
     cmpx<32>(h, l, true);
