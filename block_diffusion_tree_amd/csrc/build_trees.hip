@@ -11,7 +11,9 @@
 //      the best-first tree (Bastion, Methodology 1-2: rho products, A_hat),
 //      apply the online stop of Methodology 3, and emit the pop-order tree,
 //      the ancestor mask and the position ids.
-// Nothing waits on another block, so the grid needs no co-residency.
+// Nothing waits on another block, so the grid needs no co-residency.  The
+// latent-mixture call streams its branch rows the same way and then runs its
+// per-query stage in a second launch (mixture_kernel).
 #include "device_common.hpp"
 #include "build_params.hpp"
 #include "tree_rounds.hpp"
@@ -1140,13 +1142,23 @@ __global__ __launch_bounds__(kThreads, (R >= 16 ? 2 : 4)) void build_trees_kerne
             }
         }
     }
+    // latent mixture: the query stage runs in its own launch (mixture_kernel)
+    if constexpr (MODE == 1) return;
     if (!arrive_last(P.query_ticket + q, uint32_t(P.rows_per_query))) return;
     // The query stage is latency-bound and other queries' streams on this CU
     // wait for its results no more than it waits for them: issue ahead of
     // them (a finished stream leaves this block's waves at priority 0).
     __builtin_amdgcn_s_setprio(3);
-    if constexpr (MODE == 1) mixture_stage(P, q, smem);
-    else tree_stage<R>(P, q, smem);
+    tree_stage<R>(P, q, smem);
+}
+
+// The latent-mixture stage, one block per query, launched after the stream
+// kernel on the same stream.  A mixture stage is long (every position's
+// unions, gathers and a tree round per position); run inside the stream
+// kernel it held CU slots and issue cycles that the remaining rows needed.
+__global__ __launch_bounds__(kThreads) void mixture_kernel(BuildParams P) {
+    extern __shared__ __align__(16) char smem[];
+    mixture_stage(P, int(blockIdx.x), smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1163,7 +1175,13 @@ static hipError_t launch_one(const BuildParams &P, int smem, hipStream_t s) {
 template <typename T, int U>
 static hipError_t launch_r(const BuildParams &P, int smem, hipStream_t s) {
     // the running top-N list holds nmax keys in tree_regs(nmax) registers
-    if (P.mode == 1) return launch_one<T, U, 1, 1>(P, smem, s);
+    if (P.mode == 1) {
+        const hipError_t e = launch_one<T, U, 1, 1>(P, smem, s);
+        if (e != hipSuccess) return e;
+        const int msmem = mix_layout(P.K, P.b, P.k, P.nmax).total;
+        hipLaunchKernelGGL(mixture_kernel, dim3(unsigned(P.B)), dim3(kThreads), msmem, s, P);
+        return hipGetLastError();
+    }
     switch (tree_regs(P.nmax)) {
         case 1: return launch_one<T, U, 1>(P, smem, s);
         case 2: return launch_one<T, U, 2>(P, smem, s);
@@ -1181,8 +1199,8 @@ hipError_t bastion_launch_build(const bastion::BuildParams &P, int dtype, hipStr
     using namespace bastion;
     constexpr int U = 4;
     const int stream_smem = int(sizeof(WaveScratch<U>)) * kWavesPerBlock;
-    const int tree_smem = P.mode == 1 ? mix_layout(P.K, P.b, P.k, P.nmax).total
-                                      : tree_layout(P.b, P.k, P.nmax).total;
+    // the mixture stage has a launch of its own
+    const int tree_smem = P.mode == 1 ? 0 : tree_layout(P.b, P.k, P.nmax).total;
     const int smem = stream_smem > tree_smem ? stream_smem : tree_smem;
     if (smem_out) *smem_out = smem;
     if (dtype == BASTION_BF16) return launch_r<__bf16, U>(P, smem, s);
