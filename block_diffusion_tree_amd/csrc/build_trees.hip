@@ -556,13 +556,14 @@ __device__ void ahat_fill(const float *rho, double *ahat, int cnt) {
 // Pop-order outputs of one query (records 1..nstar in par/dep/tok/rho/ahat,
 // LDS), padding, n_nodes, qstatus and, when requested, the ancestor mask and
 // position ids (whole block).
+template <int NT = kThreads>
 __device__ void emit_tree(const BuildParams &P, int q, const int32_t *par, const int32_t *dep,
                           const int32_t *tok, const float *rho, const double *ahat, int nstar,
                           bool bad, int status) {
     const int tid = threadIdx.x, nmax = P.nmax, b = P.b;
     const int W1 = nmax + 1;
     const int64_t o = int64_t(q) * W1;
-    for (int i = tid; i < W1; i += kThreads) {
+    for (int i = tid; i < W1; i += NT) {
         const bool v = i <= nstar && !bad;
         P.parent[o + i] = v ? (i == 0 ? -1 : par[i]) : -1;
         P.depth[o + i] = v ? (i == 0 ? 0 : dep[i]) : -1;
@@ -585,7 +586,7 @@ __device__ void emit_tree(const BuildParams &P, int q, const int32_t *par, const
         // one thread per (node, mask word), each walking up from the node
         const int W = (W1 + 31) / 32;
         const int32_t pb = P.pos_base ? P.pos_base[q] : 0;
-        for (int e = tid; e < W1 * W; e += kThreads) {
+        for (int e = tid; e < W1 * W; e += NT) {
             const int i = e / W, w = e - i * W;
             uint32_t bits = 0;
             int steps = 0;
@@ -765,6 +766,7 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
 
 // Latent-mixture stage of one query (mixture.hpp): prior weights, chains and
 // their q_dep, candidate unions with q per branch, and the mixture tree.
+template <int NT>
 __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int K = P.K, b = P.b, k = P.k, C = K * k, nmax = P.nmax;
@@ -773,16 +775,16 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
     __shared__ int s_bad, s_ns, s_np;
     __shared__ uint64_t s_tau;
     if (tid == 0) s_bad = 0;
-    for (int i = tid; i < b; i += kThreads) M.cnt[i] = 0;
+    for (int i = tid; i < b; i += NT) M.cnt[i] = 0;
     __syncthreads();
     // one round trip: row statistics, row status and every position's top-k
     // ids (ids[pos * C + z * k + j] = candidate j of branch z)
-    for (int e = tid; e < K * b; e += kThreads) {
+    for (int e = tid; e < K * b; e += NT) {
         M.rowm[e] = ld_agent(P.row_ms + 2 * (r0 + e));
         M.rows[e] = ld_agent(P.row_ms + 2 * (r0 + e) + 1);
         if (ld_agent(P.row_status + r0 + e) != BASTION_Q_OK) atomicOr(&s_bad, 1);
     }
-    for (int e = tid; e < b * C; e += kThreads) {
+    for (int e = tid; e < b * C; e += NT) {
         const int pos = e / C, c = e - pos * C;
         const int z = c / k, j = c - z * k;
         M.ids[e] = ld_agent(P.topk_ids + (r0 + z * b + pos) * k + j);
@@ -803,16 +805,16 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
     const int64_t cbase = int64_t(q) * b * C;
     if (s_bad) {
         // a bad branch row: no chains, no candidates, the root alone
-        for (int e = tid; e < K * b; e += kThreads) P.chain_tokens[r0 + e] = -1;
-        for (int z = tid; z < K; z += kThreads) P.qdep[q * K + z] = 0.0;
-        for (int e = tid; e < b * C; e += kThreads) P.cand_tokens[cbase + e] = -1;
-        for (int e = tid; e < b * C * K; e += kThreads) P.cand_q[cbase * K + e] = 0.0f;
-        for (int i = tid; i < b; i += kThreads) P.cand_count[int64_t(q) * b + i] = 0;
-        if (P.mix_tree) emit_tree(P, q, M.par, M.dep, M.tok, M.rho, M.ahat, 0, true, BASTION_Q_BAD_LOGITS);
+        for (int e = tid; e < K * b; e += NT) P.chain_tokens[r0 + e] = -1;
+        for (int z = tid; z < K; z += NT) P.qdep[q * K + z] = 0.0;
+        for (int e = tid; e < b * C; e += NT) P.cand_tokens[cbase + e] = -1;
+        for (int e = tid; e < b * C * K; e += NT) P.cand_q[cbase * K + e] = 0.0f;
+        for (int i = tid; i < b; i += NT) P.cand_count[int64_t(q) * b + i] = 0;
+        if (P.mix_tree) emit_tree<NT>(P, q, M.par, M.dep, M.tok, M.rho, M.ahat, 0, true, BASTION_Q_BAD_LOGITS);
         return;
     }
     // chains: the top-1 token of every branch row (chain[z * b + i])
-    for (int e = tid; e < K * b; e += kThreads) {
+    for (int e = tid; e < K * b; e += NT) {
         const int z = e / b, i = e - z * b;
         const int t = M.ids[i * C + z * k];
         M.chain[e] = t;
@@ -822,7 +824,7 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         // unions, one position per wave at a time: sort the C tokens across
         // the lanes (ascending; padding lanes hold INT_MAX), keep the first of
         // every run of equal tokens
-        for (int pos = wv; pos < b; pos += kThreads / kWave) {
+        for (int pos = wv; pos < b; pos += NT / kWave) {
             int t = lane < C ? M.ids[pos * C + lane] : 0x7FFFFFFF;
             t = int(sort64_asc_u32(uint32_t(t)));
             const int prev = __shfl_up(t, 1);
@@ -833,7 +835,7 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         }
     } else {
         // unions, every position at once: first occurrences ...
-        for (int e = tid; e < b * C; e += kThreads) {
+        for (int e = tid; e < b * C; e += NT) {
             const int pos = e / C, c = e - pos * C;
             const int32_t *ids = M.ids + pos * C;
             const int t = ids[c];
@@ -843,7 +845,7 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         }
         __syncthreads();
         // ... then their ascending ranks
-        for (int e = tid; e < b * C; e += kThreads) {
+        for (int e = tid; e < b * C; e += NT) {
             const int pos = e / C, c = e - pos * C;
             if (M.first[e]) {
                 const int32_t *ids = M.ids + pos * C;
@@ -857,11 +859,11 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         }
     }
     __syncthreads();
-    for (int e = tid; e < b * C; e += kThreads) {
+    for (int e = tid; e < b * C; e += NT) {
         const int pos = e / C, c = e - pos * C;
         P.cand_tokens[cbase + e] = c < M.cnt[pos] ? M.ctok[e] : -1;
     }
-    for (int i = tid; i < b; i += kThreads) P.cand_count[int64_t(q) * b + i] = M.cnt[i];
+    for (int i = tid; i < b; i += NT) P.cand_count[int64_t(q) * b + i] = M.cnt[i];
     // every logit the stage needs, in batches of independent loads:
     //   chain entries  x < K*K*b: (z, z', i) -> q_i(chain z | z') into qc;
     //   candidate entries: (pos, c, z) -> q_pos(ctok | z) into cand_q
@@ -869,7 +871,7 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
     {
         constexpr int NB = 16;
         const int nch = K * K * b, tot = nch + b * C * K;
-        for (int x0 = 0; x0 < tot; x0 += NB * kThreads) {
+        for (int x0 = 0; x0 < tot; x0 += NB * NT) {
             float lv[NB];
             int lr[NB];
 #pragma unroll
@@ -877,7 +879,7 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
                 // the entry's branch row and token, without branches; an
                 // entry past the end or past its position's union re-reads
                 // token 0 of the query's first row and is discarded
-                const int x = x0 + u * kThreads + tid;
+                const int x = x0 + u * NT + tid;
                 const bool ch = x < nch;
                 const int zz = x / b, i = x - zz * b;                 // chain entry
                 const int y = x - nch;
@@ -896,7 +898,7 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
             }
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
-                const int x = x0 + u * kThreads + tid;
+                const int x = x0 + u * NT + tid;
                 const float v = lr[u] >= 0
                     ? __builtin_amdgcn_exp2f(__builtin_fmaf(lv[u], kLog2e, -scale_ref(M.rowm[lr[u]]))) /
                           M.rows[lr[u]]
@@ -910,13 +912,13 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     // q_dep: thread (z, z') forms prod_i q_i(chain z | z') in float64
-    for (int t = tid; t < K * K; t += kThreads) {
+    for (int t = tid; t < K * K; t += NT) {
         double pr = 1.0;
         for (int i = 0; i < b; ++i) pr *= double(M.qc[t * b + i]);
         M.prod[t] = pr;
     }
     __syncthreads();
-    for (int z = tid; z < K; z += kThreads) {
+    for (int z = tid; z < K; z += NT) {
         double qd = 0.0;
         for (int zp = 0; zp < K; ++zp) qd += M.w[zp] * M.prod[z * K + zp];
         P.qdep[q * K + z] = qd;
@@ -926,7 +928,7 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
     // prefetched one round ahead into the other LDS buffer
     const int nq = C * K;
     const float *cqg = P.cand_q + cbase * K;
-    for (int e = tid; e < nq; e += kThreads) M.cq[e] = ld_agent(cqg + e);
+    for (int e = tid; e < nq; e += NT) M.cq[e] = ld_agent(cqg + e);
     __syncthreads();
     int nR = 0;
     for (int d = 1; d <= b; ++d) {
@@ -936,11 +938,11 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         Mr.ctok = M.ctok + pos * C;
         float *nxt = (pos & 1) ? M.cq : M.cq2;
         // next round's table: loads now, LDS stores at the end of the round
-        constexpr int NQ = 8;   // entries per thread held in registers
+        constexpr int NQ = (2048 + NT - 1) / NT;   // entries per thread held in registers
         float pre[NQ];
 #pragma unroll
         for (int u = 0; u < NQ; ++u) {
-            const int e = u * kThreads + tid;
+            const int e = u * NT + tid;
             pre[u] = (d < b && e < nq) ? ld_agent(cqg + int64_t(d) * nq + e) : 0.0f;
         }
         const int cnt = M.cnt[pos];
@@ -974,7 +976,7 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         // above the running list's N-th) go to the buffer while it has room
         {
             const uint64_t tau = s_tau;
-            for (int idx = tid; idx < total; idx += kThreads) {
+            for (int idx = tid; idx < total; idx += NT) {
                 const int p = idx / cnt, c = idx - p * cnt;
                 const float score = mix_child(Mr, K, p, c);
                 const uint64_t key = tree_key(score, d, Mr.ctok[c], p);
@@ -989,16 +991,17 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         }
         __syncthreads();
         if (s_ns <= kMixSurv) {
-            if (s_ns > 0) nR = mix_merge<kThreads>(Mr, K, nmax, nR, s_ns);
+            if (s_ns > 0) nR = mix_merge<NT>(Mr, K, nmax, nR, s_ns);
         } else {
             // too many survivors (the list is still filling): chunk by chunk,
             // merging as the buffer fills, which raises the N-th key
             __syncthreads();
             if (tid == 0) s_ns = 0;
             __syncthreads();
-            for (int base = 0; base < total; base += kThreads) {
+            constexpr int CH = NT < kMixSurv / 2 ? NT : kMixSurv / 2;   // children per chunk
+            for (int base = 0; base < total; base += CH) {
                 const int idx = base + tid;
-                if (idx < total) {
+                if (tid < CH && idx < total) {
                     const int p = idx / cnt, c = idx - p * cnt;
                     const float score = mix_child(Mr, K, p, c);
                     const uint64_t key = tree_key(score, d, Mr.ctok[c], p);
@@ -1012,8 +1015,8 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
                 const int ns = s_ns;
                 // merge when the buffer could not take another chunk, at the
                 // end of the round, and while the list is not full
-                if (ns > 0 && (ns > kMixSurv - kThreads || base + kThreads >= total || nR < nmax)) {
-                    nR = mix_merge<kThreads>(Mr, K, nmax, nR, ns);
+                if (ns > 0 && (ns > kMixSurv - CH || base + CH >= total || nR < nmax)) {
+                    nR = mix_merge<NT>(Mr, K, nmax, nR, ns);
                     if (tid == 0) {
                         s_ns = 0;
                         s_tau = nR == nmax ? M.rkey[nmax - 1] : 0;
@@ -1024,11 +1027,11 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         }
 #pragma unroll
         for (int u = 0; u < NQ; ++u) {
-            const int e = u * kThreads + tid;
+            const int e = u * NT + tid;
             if (d < b && e < nq) nxt[e] = pre[u];
         }
         // tables larger than the prefetch (K * k > 64 with many branches)
-        for (int e = NQ * kThreads + tid; d < b && e < nq; e += kThreads)
+        for (int e = NQ * NT + tid; d < b && e < nq; e += NT)
             nxt[e] = ld_agent(cqg + int64_t(d) * nq + e);
         __syncthreads();
         if (np == 0) break;
@@ -1038,7 +1041,7 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         ahat_fill(M.rho, M.ahat, nR);
     }
     __syncthreads();
-    emit_tree(P, q, M.par, M.dep, M.tok, M.rho, M.ahat, nR, false,
+    emit_tree<NT>(P, q, M.par, M.dep, M.tok, M.rho, M.ahat, nR, false,
               nR < nmax ? BASTION_Q_EXHAUSTED : BASTION_Q_OK);
 }
 
@@ -1156,9 +1159,11 @@ __global__ __launch_bounds__(kThreads, (R >= 16 ? 2 : 4)) void build_trees_kerne
 // kernel on the same stream.  A mixture stage is long (every position's
 // unions, gathers and a tree round per position); run inside the stream
 // kernel it held CU slots and issue cycles that the remaining rows needed.
-__global__ __launch_bounds__(kThreads) void mixture_kernel(BuildParams P) {
+constexpr int kMixThreads = 1024;   // the stage has a CU to itself: 16 waves per query
+
+__global__ __launch_bounds__(kMixThreads) void mixture_kernel(BuildParams P) {
     extern __shared__ __align__(16) char smem[];
-    mixture_stage(P, int(blockIdx.x), smem);
+    mixture_stage<kMixThreads>(P, int(blockIdx.x), smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1179,7 +1184,7 @@ static hipError_t launch_r(const BuildParams &P, int smem, hipStream_t s) {
         const hipError_t e = launch_one<T, U, 1, 1>(P, smem, s);
         if (e != hipSuccess) return e;
         const int msmem = mix_layout(P.K, P.b, P.k, P.nmax).total;
-        hipLaunchKernelGGL(mixture_kernel, dim3(unsigned(P.B)), dim3(kThreads), msmem, s, P);
+        hipLaunchKernelGGL(mixture_kernel, dim3(unsigned(P.B)), dim3(kMixThreads), msmem, s, P);
         return hipGetLastError();
     }
     switch (tree_regs(P.nmax)) {
