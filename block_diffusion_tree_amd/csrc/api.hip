@@ -213,8 +213,9 @@ int32_t bastion_mixture_score(const void *branch_logits, int32_t dtype, const fl
         !mix->cand_tokens || !mix->cand_q || !mix->row_max || !mix->row_sum)
         return BASTION_EINVAL;
     if (tree && !tree_out_ok(tree, false)) return BASTION_EINVAL;
-    // the query stage keeps one position's candidates and the running list in LDS
-    if (mix_layout(K, b, k, nmax).total > 65536) return BASTION_EUNSUPPORTED;
+    // the query stage keeps every position's candidates and q tables and the
+    // running list in the LDS of one CU
+    if (mix_layout(K, b, k, nmax).total > kMixMaxLds) return BASTION_EUNSUPPORTED;
     const int64_t rows = int64_t(B) * K * b;
     const int S = plan_segments(rows, V, dtype);
     const Layout L = layout(rows, k, S);

@@ -903,13 +903,15 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
                     ? __builtin_amdgcn_exp2f(__builtin_fmaf(lv[u], kLog2e, -scale_ref(M.rowm[lr[u]]))) /
                           M.rows[lr[u]]
                     : 0.0f;
-                if (x < nch) M.qc[x] = v;
-                else if (x < tot) P.cand_q[cbase * K + (x - nch)] = v;
+                if (x < nch) {
+                    M.qc[x] = v;
+                } else if (x < tot) {
+                    M.cq[x - nch] = v;
+                    P.cand_q[cbase * K + (x - nch)] = v;
+                }
             }
         }
     }
-    // the cand_q stores are read back by this block below
-    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     // q_dep: thread (z, z') forms prod_i q_i(chain z | z') in float64
     for (int t = tid; t < K * K; t += NT) {
@@ -924,27 +926,13 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         P.qdep[q * K + z] = qd;
     }
     if (!P.mix_tree) return;
-    // the tree, round by round; a round's q table (C x K) comes from cand_q,
-    // prefetched one round ahead into the other LDS buffer
-    const int nq = C * K;
-    const float *cqg = P.cand_q + cbase * K;
-    for (int e = tid; e < nq; e += NT) M.cq[e] = ld_agent(cqg + e);
-    __syncthreads();
+    // the tree, round by round (each position's q table is in LDS)
     int nR = 0;
     for (int d = 1; d <= b; ++d) {
         const int pos = d - 1;
         MixLds Mr = M;
-        Mr.cq = (pos & 1) ? M.cq2 : M.cq;
+        Mr.cq = M.cq + pos * C * K;
         Mr.ctok = M.ctok + pos * C;
-        float *nxt = (pos & 1) ? M.cq : M.cq2;
-        // next round's table: loads now, LDS stores at the end of the round
-        constexpr int NQ = (2048 + NT - 1) / NT;   // entries per thread held in registers
-        float pre[NQ];
-#pragma unroll
-        for (int u = 0; u < NQ; ++u) {
-            const int e = u * NT + tid;
-            pre[u] = (d < b && e < nq) ? ld_agent(cqg + int64_t(d) * nq + e) : 0.0f;
-        }
         const int cnt = M.cnt[pos];
         // tree round d: the parents are the depth-(d-1) entries, in order
         if (d == 1) {
@@ -959,6 +947,7 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
                 const uint64_t m = __ballot(v);
                 if (v) {
                     const int pp = np + popc64(m & lt);
+#pragma unroll 8
                     for (int z = 0; z < K; ++z) M.ptab[pp * K + z] = M.rr[e * K + z];
                 }
                 np += popc64(m);
@@ -1025,14 +1014,6 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
                 }
             }
         }
-#pragma unroll
-        for (int u = 0; u < NQ; ++u) {
-            const int e = u * NT + tid;
-            if (d < b && e < nq) nxt[e] = pre[u];
-        }
-        // tables larger than the prefetch (K * k > 64 with many branches)
-        for (int e = NQ * NT + tid; d < b && e < nq; e += NT)
-            nxt[e] = ld_agent(cqg + int64_t(d) * nq + e);
         __syncthreads();
         if (np == 0) break;
     }
@@ -1184,6 +1165,11 @@ static hipError_t launch_r(const BuildParams &P, int smem, hipStream_t s) {
         const hipError_t e = launch_one<T, U, 1, 1>(P, smem, s);
         if (e != hipSuccess) return e;
         const int msmem = mix_layout(P.K, P.b, P.k, P.nmax).total;
+        if (msmem > 65536) {
+            const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void *>(mixture_kernel),
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize, msmem);
+            if (ea != hipSuccess) return ea;
+        }
         hipLaunchKernelGGL(mixture_kernel, dim3(unsigned(P.B)), dim3(kMixThreads), msmem, s, P);
         return hipGetLastError();
     }

@@ -21,9 +21,8 @@
 //      round d merging the children of its depth-(d-1) nodes.  A child's key
 //      carries its parent's rank among the depth-(d-1) entries, which is
 //      best-first's parent-order tie-break.  Candidates that beat the list's
-//      N-th key are buffered and merged kMixSurv at a time.  A round reads
-//      its position's q table from the cand_q output, prefetched into LDS
-//      one round ahead.
+//      N-th key are buffered and merged kMixSurv at a time.  The rounds read
+//      their positions' q tables from LDS, where the gathers left them.
 #pragma once
 
 #include "device_common.hpp"
@@ -32,6 +31,7 @@
 namespace bastion {
 
 constexpr int kMixSurv = 512;   // survivors buffered between merges
+constexpr int kMixMaxLds = 160 * 1024;   // LDS of one CU
 
 struct MixLayout {
     int w, wq, prod, rowm, rows, chain, ids, first, ctok, cnt, qc, cq, cq2, rkey, rr, nkey, nr, ptab, skey,
@@ -40,9 +40,12 @@ struct MixLayout {
 
 __host__ __device__ inline int mix_align16(int x) { return (x + 15) & ~15; }
 
-// Three regions: arrays live through the whole stage; arrays used only
-// before the tree rounds (every position's ids, first-occurrence flags, the
-// chains' q); arrays used only by the rounds.  The last two share space.
+// Three regions: arrays live through the whole stage (among them every
+// position's q table, written by the gathers and read by the rounds); arrays
+// used only before the tree rounds (every position's ids, first-occurrence
+// flags, the chains' q); arrays used only by the rounds.  The last two share
+// space.  The stage has a launch of its own, one block per CU, so the
+// layout may use up to kMixMaxLds bytes.
 __host__ __device__ inline MixLayout mix_layout(int K, int b, int k, int nmax) {
     MixLayout L;
     const int C = K * k, nn = nmax + 2;
@@ -62,6 +65,9 @@ __host__ __device__ inline MixLayout mix_layout(int K, int b, int k, int nmax) {
     L.tok = o;   o = mix_align16(o + 4 * nn);
     L.rho = o;   o = mix_align16(o + 4 * nn);
     L.ahat = o;  o = mix_align16(o + 8 * nn);
+    // every position's q table, written by the gathers, read by the rounds
+    L.cq = o;    o = mix_align16(o + 4 * b * C * K);
+    L.cq2 = L.cq;
     // before the rounds
     int a = o;
     L.ids = a;   a = mix_align16(a + 4 * b * C);   // every position's top-k ids
@@ -69,8 +75,6 @@ __host__ __device__ inline MixLayout mix_layout(int K, int b, int k, int nmax) {
     L.qc = a;    a = mix_align16(a + 4 * K * K * b); // q_i(chain z | z')
     // the rounds
     int r = o;
-    L.cq = r;    r = mix_align16(r + 4 * C * K);   // one position's q table, two buffers
-    L.cq2 = r;   r = mix_align16(r + 4 * C * K);
     L.rkey = r;  r = mix_align16(r + 8 * nmax);
     L.rr = r;    r = mix_align16(r + 4 * nmax * K);
     L.nkey = r;  r = mix_align16(r + 8 * nmax);
@@ -128,6 +132,7 @@ __device__ __forceinline__ MixLds mix_lds(char *smem, const MixLayout &L) {
 // fl32(r_z(parent) * q(c | z))
 __device__ __forceinline__ float mix_child(const MixLds &M, int K, int p, int c) {
     float acc = 0.0f;
+#pragma unroll 8
     for (int z = 0; z < K; ++z)
         acc = __builtin_fmaf(M.wq[z], __fmul_rn(M.ptab[p * K + z], M.cq[c * K + z]), acc);
     return acc;
@@ -155,14 +160,26 @@ __device__ int mix_merge(const MixLds &M, int K, int nmax, int nR, int ns) {
             }
             rank = lo;
         }
-        for (int s = 0; s < ns; ++s) rank += M.skey[s] > x ? 1 : 0;
+        // survivors above x: eight independent counts keep eight LDS reads
+        // in flight
+        int cnt8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        int s = 0;
+        for (; s + 8 <= ns; s += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) cnt8[u] += M.skey[s + u] > x ? 1 : 0;
+        }
+        for (; s < ns; ++s) cnt8[0] += M.skey[s] > x ? 1 : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rank += cnt8[u];
         if (rank < nmax) {
             M.nkey[rank] = x;
             if (e < nR) {
+#pragma unroll 8
                 for (int z = 0; z < K; ++z) M.nr[rank * K + z] = M.rr[e * K + z];
             } else {
                 const int info = M.sinfo[e - nR];
                 const int p = info >> 16, c = info & 0xFFFF;
+#pragma unroll 8
                 for (int z = 0; z < K; ++z)
                     M.nr[rank * K + z] = __fmul_rn(M.ptab[p * K + z], M.cq[c * K + z]);
             }
@@ -172,6 +189,7 @@ __device__ int mix_merge(const MixLds &M, int K, int nmax, int nR, int ns) {
     const int n = nE < nmax ? nE : nmax;
     for (int i = tid; i < n; i += THREADS) {
         M.rkey[i] = M.nkey[i];
+#pragma unroll 8
         for (int z = 0; z < K; ++z) M.rr[i * K + z] = M.nr[i * K + z];
     }
     __syncthreads();
