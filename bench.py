@@ -13,7 +13,9 @@ rotating 5 GB batches.
 Prints one JSON line.  `value` is trees per second over the timed steps.
 `roofline` is the fused kernel's algorithmic bytes per launch (every logit
 read once plus every output written once) over its mean launch time,
-measured with HIP events recorded on the stream the kernel runs on.
+measured with HIP events recorded on the stream the kernel runs on (for the
+mixture call, the span of its two launches: the stream kernel and the
+per-query stage).
 `cpu_baseline` times the CPU reference on the same batch (host copy).
 """
 from __future__ import annotations
@@ -198,7 +200,9 @@ def main():
                    "logits_dtype": wl.dtype, "rotating_buffers": nbuf},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "build_trees_kernel (mixture mode)" if mixture else "build_trees_kernel", "alg_bytes_per_launch": alg_bytes,
+                     "kernel": ("build_trees_kernel (mixture mode) + mixture_kernel: the two launches "
+                                "of one call, timed together" if mixture else "build_trees_kernel"),
+                     "alg_bytes_per_launch": alg_bytes,
                      "launch_us_mean": mean_ms * 1e3,
                      "launch_us_p50": float(np.median(launch_ms)) * 1e3,
                      "launch_us_p10": float(np.percentile(launch_ms, 10)) * 1e3,
