@@ -39,6 +39,7 @@ constexpr size_t kRowTicketWords = 49152;            // per-row counters
 constexpr size_t kQueryTicketBase = kRowTicketWords;  // per-query counters
 constexpr size_t kTicketBytes = kTicketWords * 4;
 constexpr int kMaxSegments = 64;
+constexpr int64_t kResidentBlocks = 1024;   // stream blocks resident at once
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -166,6 +167,13 @@ int32_t bastion_build_trees(const void *logits, int32_t dtype, int32_t B, int32_
     P.rows_per_query = b;
     P.is_bf16 = dtype == BASTION_BF16;
     P.row_ms = nullptr;
+    // the stream grid fills the machine more than once (256 CUs x 4 blocks):
+    // trees in a launch of their own
+    P.split_trees = rows * S > kResidentBlocks ? 1 : 0;
+    {
+        const char *env = getenv("BASTION_SPLIT_TREES");
+        if (env) P.split_trees = atoi(env) != 0;
+    }
     return to_status(bastion_launch_build(P, dtype, static_cast<hipStream_t>(stream), nullptr));
 }
 

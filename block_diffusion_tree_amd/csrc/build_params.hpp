@@ -39,6 +39,7 @@ struct BuildParams {
     int32_t *cand_count, *cand_tokens;
     float *cand_q;
     int mix_tree;         // 1: build the mixture tree into parent/depth/...
+    int split_trees;      // 1: the trees run in a launch of their own (mode 0)
 };
 
 }  // namespace bastion

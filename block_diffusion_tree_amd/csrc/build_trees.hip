@@ -1128,6 +1128,8 @@ __global__ __launch_bounds__(kThreads, (R >= 16 ? 2 : 4)) void build_trees_kerne
     }
     // latent mixture: the query stage runs in its own launch (mixture_kernel)
     if constexpr (MODE == 1) return;
+    // more blocks than fit the machine at once: trees in their own launch
+    if (P.split_trees) return;
     if (!arrive_last(P.query_ticket + q, uint32_t(P.rows_per_query))) return;
     // The query stage is latency-bound and other queries' streams on this CU
     // wait for its results no more than it waits for them: issue ahead of
@@ -1147,6 +1149,16 @@ __global__ __launch_bounds__(kMixThreads) void mixture_kernel(BuildParams P) {
     mixture_stage<kMixThreads>(P, int(blockIdx.x), smem);
 }
 
+// The trees of a call whose stream grid does not fit the machine at once,
+// one block per query, launched after the stream kernel on the same stream.
+// Run by the last row block of a query inside the stream grid, a tree would
+// hold a block slot while rows of later queries wait to be dispatched.
+template <int R>
+__global__ __launch_bounds__(kThreads) void tree_kernel(BuildParams P) {
+    extern __shared__ __align__(16) char smem[];
+    tree_stage<R>(P, int(blockIdx.x), smem);
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launch helpers (called from api.hip).
 // ---------------------------------------------------------------------------
@@ -1155,6 +1167,15 @@ static hipError_t launch_one(const BuildParams &P, int smem, hipStream_t s) {
     auto kern = build_trees_kernel<T, U, R, MODE>;
     const int64_t grid = int64_t(P.B) * P.rows_per_query * P.S;
     hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), smem, s, P);
+    if (MODE == 0 && P.split_trees) {
+        const int tsm = tree_layout(P.b, P.k, P.nmax).total;
+        if (tsm > 65536) {
+            const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void *>(tree_kernel<R>),
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize, tsm);
+            if (ea != hipSuccess) return ea;
+        }
+        hipLaunchKernelGGL(tree_kernel<R>, dim3(unsigned(P.B)), dim3(kThreads), tsm, s, P);
+    }
     return hipGetLastError();
 }
 
@@ -1191,7 +1212,7 @@ hipError_t bastion_launch_build(const bastion::BuildParams &P, int dtype, hipStr
     constexpr int U = 4;
     const int stream_smem = int(sizeof(WaveScratch<U>)) * kWavesPerBlock;
     // the mixture stage has a launch of its own
-    const int tree_smem = P.mode == 1 ? 0 : tree_layout(P.b, P.k, P.nmax).total;
+    const int tree_smem = (P.mode == 1 || P.split_trees) ? 0 : tree_layout(P.b, P.k, P.nmax).total;
     const int smem = stream_smem > tree_smem ? stream_smem : tree_smem;
     if (smem_out) *smem_out = smem;
     if (dtype == BASTION_BF16) return launch_r<__bf16, U>(P, smem, s);

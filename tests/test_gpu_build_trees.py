@@ -93,6 +93,33 @@ def test_sweep_logits_with_peaks_online():
     assert n.min() > 4 and n.max() < 256
 
 
+def test_trees_in_their_own_launch():
+    """Stream grids larger than the machine (here 1280 rows) build the trees
+    in a launch of their own, with the online budget stop."""
+    wl = synth.scaled(synth.WORKLOADS["sweep"], B=80, V=20000)
+    x = gc.device_logits(wl)
+    cost = cost_table(wl.B, wl.nmax, wl.seed, synth.LATENCY_A100)
+    g, _ = gc.run_and_check(x, wl.k, wl.nmax, nmin=1, cost=cost, l_ar=1.0)
+    g2 = binding.build_trees(x, k=wl.k, nmax=wl.nmax, cost=cost)
+    torch.cuda.synchronize()
+    for f in g:
+        assert torch.equal(g[f], g2[f]), f
+
+
+def test_split_and_fused_trees_agree():
+    wl = synth.scaled(synth.WORKLOADS["main"], B=4, b=16, V=30011, nmax=64)
+    x = gc.device_logits(wl, seed=9)
+    fused = binding.build_trees(x, k=wl.k, nmax=wl.nmax)
+    os.environ["BASTION_SPLIT_TREES"] = "1"
+    try:
+        split = binding.build_trees(x, k=wl.k, nmax=wl.nmax)
+    finally:
+        os.environ.pop("BASTION_SPLIT_TREES", None)
+    torch.cuda.synchronize()
+    for f in fused:
+        assert torch.equal(fused[f], split[f]), f
+
+
 def test_bad_rows_and_padding():
     wl = synth.scaled(synth.WORKLOADS["tiny"], B=5, b=3, V=2000, nmax=12)
     x = synth.make_logits(wl)
