@@ -40,6 +40,7 @@ constexpr size_t kQueryTicketBase = kRowTicketWords;  // per-query counters
 constexpr size_t kTicketBytes = kTicketWords * 4;
 constexpr int kMaxSegments = 64;
 constexpr int64_t kResidentBlocks = 1024;   // stream blocks resident at once
+constexpr int kFewQueries = 4;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -50,15 +51,18 @@ struct Layout {
     int S;
 };
 
-// Segments per row: enough blocks to cover the machine (256 CUs, four
-// resident blocks each) without making a segment shorter than one 16-byte
-// load per thread.  BASTION_SEGMENTS overrides (tuning).
+// Segments per row.  Enough blocks to cover the machine: four resident
+// blocks on each of the 256 CUs, or one per CU when the whole input is small
+// (at most 16 MiB), where every block's fixed latency (start, merge,
+// hand-off) outweighs its streaming.  No segment shorter than 16 KiB (four
+// 16-byte loads per thread).  BASTION_SEGMENTS overrides (tuning).
 int plan_segments(int64_t rows, int V, int dtype) {
-    int S = int((1024 + rows - 1) / rows);
+    const int64_t row_bytes = int64_t(V) * esize(dtype);
+    const int64_t target = rows * row_bytes <= (int64_t(16) << 20) ? 256 : 1024;
+    int S = int((target + rows - 1) / rows);
     const char *env = getenv("BASTION_SEGMENTS");
     if (env && atoi(env) > 0) S = atoi(env);
-    const int64_t row_bytes = int64_t(V) * esize(dtype);
-    const int64_t by_size = row_bytes / 4096;
+    const int64_t by_size = row_bytes / (env && atoi(env) > 0 ? 4096 : 16384);
     if (S > by_size) S = int(by_size);
     if (S > kMaxSegments) S = kMaxSegments;
     if (S < 1) S = 1;
@@ -167,9 +171,11 @@ int32_t bastion_build_trees(const void *logits, int32_t dtype, int32_t B, int32_
     P.rows_per_query = b;
     P.is_bf16 = dtype == BASTION_BF16;
     P.row_ms = nullptr;
-    // the stream grid fills the machine more than once (256 CUs x 4 blocks):
-    // trees in a launch of their own
-    P.split_trees = rows * S > kResidentBlocks ? 1 : 0;
+    // trees in a launch of their own (one block of 16 waves per query) when
+    // the stream grid fills the machine more than once (256 CUs x 4 blocks),
+    // where a tree would hold a slot that later rows wait for, and when there
+    // are so few queries that no stream is left for the trees to overlap
+    P.split_trees = (rows * S > kResidentBlocks || B <= kFewQueries) ? 1 : 0;
     {
         const char *env = getenv("BASTION_SPLIT_TREES");
         if (env) P.split_trees = atoi(env) != 0;

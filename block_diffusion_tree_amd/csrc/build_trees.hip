@@ -431,7 +431,7 @@ struct TreeLayout {
     int pkey, ppar, prho, plrank, ppop, hist, plvl, q0col, fwork, total;
 };
 
-__host__ __device__ inline TreeLayout tree_layout(int b, int k, int nmax) {
+__host__ __device__ inline TreeLayout tree_layout(int b, int k, int nmax, int threads = kThreads) {
     TreeLayout L;
     const int nn = nmax + 2;
     const int cap = pool_cap(tree_regs(nmax));
@@ -458,7 +458,7 @@ __host__ __device__ inline TreeLayout tree_layout(int b, int k, int nmax) {
     L.plvl = o; o = align16(o + (cap > 0 ? 4 * kLvlFloats : 0));
     L.q0col = o; o = align16(o + 3 * 4 * kColLen);   // FamilyCols q0, q1n, t0
     // FamilyWork: cmask, gpre, wtot, flag
-    L.fwork = o; o = align16(o + 8 * kFamGroups + 4 * kFamGroups + 4 * kFamRounds * (kThreads / kWave) + 16);
+    L.fwork = o; o = align16(o + 8 * kFamGroups + 4 * kFamGroups + 4 * kFamRounds * (threads / kWave) + 16);
     L.total = o;
     return L;
 }
@@ -605,10 +605,10 @@ __device__ void emit_tree(const BuildParams &P, int q, const int32_t *par, const
     }
 }
 
-template <int G>
+template <int G, int NT = kThreads>
 __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const TreeLayout TL = tree_layout(P.b, P.k, P.nmax);
+    const TreeLayout TL = tree_layout(P.b, P.k, P.nmax, NT);
     RoundsLds S;
     S.qtab = reinterpret_cast<float *>(smem + TL.qtab);
     S.ttab = reinterpret_cast<int32_t *>(smem + TL.ttab);
@@ -634,7 +634,7 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
     int32_t *ft0 = reinterpret_cast<int32_t *>(fq1n + kColLen);
     // the row status loads go out with the table loads: one round trip
     const int32_t rst = tid < b ? ld_agent(P.row_status + int64_t(q) * b + tid) : int32_t(BASTION_Q_OK);
-    for (int e = tid; e < b * kp; e += kThreads) {
+    for (int e = tid; e < b * kp; e += NT) {
         const int d = e / kp, j = e - d * kp;
         const float qv = j < k ? ld_agent(P.topk_q + tk0 + d * k + j) : 0.0f;
         const int32_t tv = j < k ? ld_agent(P.topk_ids + tk0 + d * k + j) : 0;
@@ -646,7 +646,7 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
         }
         if (j == 1 && d >= 1) fq1n[d - 1] = qv;
     }
-    for (int d = tid; d < kColLen; d += kThreads) {
+    for (int d = tid; d < kColLen; d += NT) {
         if (d >= b) {
             fq0[d] = 0.0f;
             ft0[d] = 0;
@@ -657,17 +657,17 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
     FW.cmask = reinterpret_cast<uint64_t *>(smem + TL.fwork);
     FW.gpre = reinterpret_cast<int32_t *>(FW.cmask + kFamGroups);
     FW.wtot = FW.gpre + kFamGroups;
-    FW.flag = FW.wtot + kFamRounds * (kThreads / kWave);
+    FW.flag = FW.wtot + kFamRounds * (NT / kWave);
     if (kPoolCap > 0) {
         uint32_t *hist = reinterpret_cast<uint32_t *>(smem + TL.hist);
         int32_t *pop = reinterpret_cast<int32_t *>(smem + TL.ppop);
-        for (int i = tid; i < kHistBins + kWave; i += kThreads) hist[i] = 0u;
-        for (int i = tid; i < kPoolCap + kPoolPad + kWave; i += kThreads) pop[i] = 0;
+        for (int i = tid; i < kHistBins + kWave; i += NT) hist[i] = 0u;
+        for (int i = tid; i < kPoolCap + kPoolPad + kWave; i += NT) pop[i] = 0;
         if (tid == 0) FW.flag[0] = 0;
     }
     const bool online = P.cost != nullptr;
     if (online)
-        for (int e = tid; e <= nmax; e += kThreads)
+        for (int e = tid; e <= nmax; e += NT)
             S.cost[e] = P.cost[int64_t(q) * P.cost_qstride + e];
     if (tid == 0) s_bad = 0;
     __syncthreads();
@@ -691,10 +691,10 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
         F.q1n = fq1n;
         F.t0 = ft0;
         FamRegs FR;
-        const float bound = family_bound<kThreads>(S.qtab, S.ttab, F, b, k, kp, nmax, PL.hist, lvl, FR);
+        const float bound = family_bound<NT>(S.qtab, S.ttab, F, b, k, kp, nmax, PL.hist, lvl, FR);
         // the family usually holds every node at or above the bound; if not,
         // one wave enumerates them level by level
-        const int nf = family_select<kThreads>(PL, S.qtab, S.ttab, F, FW, FR, b, k, kp, bound,
+        const int nf = family_select<NT>(PL, S.qtab, S.ttab, F, FW, FR, b, k, kp, bound,
                                                kPoolCap, lvl);
         if (nf >= 1 && nf <= kPoolCap) {
             FamGeom FG;
@@ -711,7 +711,7 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
             FG.ttab = S.ttab;
             FG.cmask = FW.cmask;
             FG.gpre = FW.gpre;
-            cnt = family_rank<kThreads>(PL, FG, nf, nmax, kPoolCap, S.par, S.dep, S.tok, S.rho);
+            cnt = family_rank<NT>(PL, FG, nf, nmax, kPoolCap, S.par, S.dep, S.tok, S.rho);
         } else if (nf == -1) {
             if (wv == 0) {
                 const int n = pool_enumerate(PL, S.qtab, S.ttab, b, k, kp, bound, kPoolCap);
@@ -719,7 +719,7 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
             }
             __syncthreads();
             const int n = s_pool;
-            if (n >= 1) cnt = pool_rank<kThreads>(PL, n, nmax, S.par, S.dep, S.tok, S.rho);
+            if (n >= 1) cnt = pool_rank<NT>(PL, n, nmax, S.par, S.dep, S.tok, S.rho);
         }
         __syncthreads();
     }
@@ -761,7 +761,7 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
     __syncthreads();
     const int nstar = bad ? 0 : s_nstar;
     const int status = bad ? BASTION_Q_BAD_LOGITS : s_status;
-    emit_tree(P, q, S.par, S.dep, S.tok, S.rho, S.ahat, nstar, bad, status);
+    emit_tree<NT>(P, q, S.par, S.dep, S.tok, S.rho, S.ahat, nstar, bad, status);
 }
 
 // Latent-mixture stage of one query (mixture.hpp): prior weights, chains and
@@ -1153,10 +1153,16 @@ __global__ __launch_bounds__(kMixThreads) void mixture_kernel(BuildParams P) {
 // one block per query, launched after the stream kernel on the same stream.
 // Run by the last row block of a query inside the stream grid, a tree would
 // hold a block slot while rows of later queries wait to be dispatched.
+// The block has a CU to itself, so it takes 16 waves (8 with the largest
+// running lists, whose registers would not fit 16): the stage's comparison
+// and walk loops are latency-bound at one wave per SIMD.
 template <int R>
-__global__ __launch_bounds__(kThreads) void tree_kernel(BuildParams P) {
+constexpr int tree_threads() { return R >= 16 ? 512 : 1024; }
+
+template <int R>
+__global__ __launch_bounds__(tree_threads<R>()) void tree_kernel(BuildParams P) {
     extern __shared__ __align__(16) char smem[];
-    tree_stage<R>(P, int(blockIdx.x), smem);
+    tree_stage<R, tree_threads<R>()>(P, int(blockIdx.x), smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1168,13 +1174,13 @@ static hipError_t launch_one(const BuildParams &P, int smem, hipStream_t s) {
     const int64_t grid = int64_t(P.B) * P.rows_per_query * P.S;
     hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), smem, s, P);
     if (MODE == 0 && P.split_trees) {
-        const int tsm = tree_layout(P.b, P.k, P.nmax).total;
+        const int tsm = tree_layout(P.b, P.k, P.nmax, tree_threads<R>()).total;
         if (tsm > 65536) {
             const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void *>(tree_kernel<R>),
                                                       hipFuncAttributeMaxDynamicSharedMemorySize, tsm);
             if (ea != hipSuccess) return ea;
         }
-        hipLaunchKernelGGL(tree_kernel<R>, dim3(unsigned(P.B)), dim3(kThreads), tsm, s, P);
+        hipLaunchKernelGGL(tree_kernel<R>, dim3(unsigned(P.B)), dim3(tree_threads<R>()), tsm, s, P);
     }
     return hipGetLastError();
 }

@@ -106,8 +106,15 @@ def test_trees_in_their_own_launch():
         assert torch.equal(g[f], g2[f]), f
 
 
-def test_split_and_fused_trees_agree():
-    wl = synth.scaled(synth.WORKLOADS["main"], B=4, b=16, V=30011, nmax=64)
+@pytest.mark.parametrize("shape", [
+    dict(B=4, b=16, V=30011, k=8, nmax=64),        # 16 waves per tree
+    dict(B=3, b=3, V=4099, k=32, nmax=200),        # widest candidate lists
+    dict(B=2, b=32, V=777, k=2, nmax=1023),        # largest list: 8 waves per tree
+])
+def test_split_and_fused_trees_agree(shape):
+    """The trees' own launch (more waves per tree) builds the same trees as
+    the last row block of each query."""
+    wl = synth.scaled(synth.WORKLOADS["main"], **shape)
     x = gc.device_logits(wl, seed=9)
     fused = binding.build_trees(x, k=wl.k, nmax=wl.nmax)
     os.environ["BASTION_SPLIT_TREES"] = "1"
