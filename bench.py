@@ -201,7 +201,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": ("build_trees_kernel (mixture mode) + mixture_kernel: the two launches "
-                                "of one call, timed together" if mixture else "build_trees_kernel"),
+                                "of one call, timed together" if mixture else
+                                "build_trees_kernel, plus tree_kernel when the call builds its trees "
+                                "in a launch of their own; the call's launches timed together"),
                      "alg_bytes_per_launch": alg_bytes,
                      "launch_us_mean": mean_ms * 1e3,
                      "launch_us_p50": float(np.median(launch_ms)) * 1e3,
