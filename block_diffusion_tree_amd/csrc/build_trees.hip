@@ -770,7 +770,7 @@ template <int NT>
 __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int K = P.K, b = P.b, k = P.k, C = K * k, nmax = P.nmax;
-    const MixLds M = mix_lds(smem, mix_layout(K, b, k, nmax));
+    MixLds M = mix_lds(smem, mix_layout(K, b, k, nmax), C);
     const int64_t r0 = int64_t(q) * K * b;
     __shared__ int s_bad, s_ns, s_np;
     __shared__ uint64_t s_tau;
@@ -906,8 +906,13 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
                 if (x < nch) {
                     M.qc[x] = v;
                 } else if (x < tot) {
-                    M.cq[x - nch] = v;
-                    P.cand_q[cbase * K + (x - nch)] = v;
+                    // LDS: candidate fastest, so that a wave's lanes (one
+                    // candidate each) read consecutive words in the rounds
+                    const int y = x - nch;
+                    const int pc = y / K, zc = y - pc * K;
+                    const int pos = pc / C, c = pc - pos * C;
+                    M.cq[(pos * K + zc) * C + c] = v;
+                    P.cand_q[cbase * K + y] = v;
                 }
             }
         }
@@ -926,64 +931,100 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         P.qdep[q * K + z] = qd;
     }
     if (!P.mix_tree) return;
-    // the tree, round by round (each position's q table is in LDS)
+    // the tree, round by round (each position's q table is in LDS).  The
+    // running list and the parent table are double-buffered: a merge writes
+    // the other buffers, which then become the current ones.
+    MixLds L = M;
     int nR = 0;
+    int np = 1;               // round 1: the root
+    bool scan = false;        // parents to be found by a scan of the list
+    __shared__ int s_npn;
+    for (int i = tid; i < nmax + kMixSurv; i += NT) L.rankb[i] = 0;
+    if (tid < K) L.ptab[tid] = 1.0f;
     for (int d = 1; d <= b; ++d) {
         const int pos = d - 1;
-        MixLds Mr = M;
-        Mr.cq = M.cq + pos * C * K;
-        Mr.ctok = M.ctok + pos * C;
+        L.cq = M.cq + pos * C * K;
+        L.ctok = M.ctok + pos * C;
         const int cnt = M.cnt[pos];
-        // tree round d: the parents are the depth-(d-1) entries, in order
-        if (d == 1) {
-            if (tid < K) M.ptab[tid] = 1.0f;
-            if (tid == 0) s_np = 1;
-        } else if (wv == 0) {
+        if (scan && wv == 0) {
+            // after a round merged in several parts: the parents are the
+            // depth-(d-1) entries, in list order
             const uint64_t lt = lanemask_lt();
-            int np = 0;
+            int n = 0;
             for (int e0 = 0; e0 < nR; e0 += kWave) {
                 const int e = e0 + lane;
-                const bool v = e < nR && tree_key_depth(M.rkey[e]) == d - 1;
+                const bool v = e < nR && tree_key_depth(L.rkey[e]) == d - 1;
                 const uint64_t m = __ballot(v);
                 if (v) {
-                    const int pp = np + popc64(m & lt);
+                    const int pp = n + popc64(m & lt);
 #pragma unroll 8
-                    for (int z = 0; z < K; ++z) M.ptab[pp * K + z] = M.rr[e * K + z];
+                    for (int z = 0; z < K; ++z) L.ptab[pp * K + z] = L.rr[e * K + z];
                 }
-                np += popc64(m);
+                n += popc64(m);
             }
-            if (lane == 0) s_np = np;
+            if (lane == 0) s_np = n;
         }
         if (tid == 0) {
             s_ns = 0;
-            s_tau = nR == nmax ? M.rkey[nmax - 1] : 0;
+            s_npn = 0;
+            s_tau = nR == nmax ? L.rkey[nmax - 1] : 0;
         }
         __syncthreads();
-        const int np = s_np;
+        if (scan) np = s_np;
+        if (np == 0) break;
         const int total = np * cnt;
         // one pass over all children without barriers: the survivors (keys
-        // above the running list's N-th) go to the buffer while it has room
+        // above the running list's N-th) go to the buffer while it has room,
+        // one buffer reservation per wave
         {
             const uint64_t tau = s_tau;
-            for (int idx = tid; idx < total; idx += NT) {
-                const int p = idx / cnt, c = idx - p * cnt;
-                const float score = mix_child(Mr, K, p, c);
-                const uint64_t key = tree_key(score, d, Mr.ctok[c], p);
-                if (key > tau) {
-                    const int slot = atomicAdd(&s_ns, 1);
-                    if (slot < kMixSurv) {
-                        M.skey[slot] = key;
-                        M.sinfo[slot] = (p << 16) | c;
+            const uint64_t lt = lanemask_lt();
+            // survivors of one wave step: one buffer reservation per wave
+            auto keep = [&](bool sv, uint64_t key, int info) {
+                const uint64_t m = __ballot(sv);
+                if (m) {
+                    int slot0 = 0;
+                    if (lane == 0) slot0 = atomicAdd(&s_ns, popc64(m));
+                    slot0 = __shfl(slot0, 0);
+                    const int slot = slot0 + popc64(m & lt);
+                    if (sv && slot < kMixSurv) {
+                        L.skey[slot] = key;
+                        L.sinfo[slot] = info;
                     }
                 }
+            };
+            for (int base = 0; base < total; base += NT) {
+                const int idx = base + tid;
+                bool sv = false;
+                uint64_t key = 0;
+                int info = 0;
+                if (idx < total) {
+                    const int p = idx / cnt, c = idx - p * cnt;
+                    const float score = mix_child(L, K, p, c);
+                    key = tree_key(score, d, L.ctok[c], p);
+                    sv = key > tau;
+                    info = (p << 16) | c;
+                }
+                keep(sv, key, info);
             }
         }
         __syncthreads();
-        if (s_ns <= kMixSurv) {
-            if (s_ns > 0) nR = mix_merge<NT>(Mr, K, nmax, nR, s_ns);
+        const int ns = s_ns;
+        if (ns <= kMixSurv) {
+            scan = false;
+            np = 0;
+            if (ns > 0) {
+                nR = mix_merge<NT>(L, K, nmax, nR, ns, true, &s_npn);
+                np = s_npn;
+                swap_list(L);
+                float *t = L.ptab;
+                L.ptab = L.ptab2;
+                L.ptab2 = t;
+            }
         } else {
             // too many survivors (the list is still filling): chunk by chunk,
             // merging as the buffer fills, which raises the N-th key
+            scan = true;
             __syncthreads();
             if (tid == 0) s_ns = 0;
             __syncthreads();
@@ -992,31 +1033,32 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
                 const int idx = base + tid;
                 if (tid < CH && idx < total) {
                     const int p = idx / cnt, c = idx - p * cnt;
-                    const float score = mix_child(Mr, K, p, c);
-                    const uint64_t key = tree_key(score, d, Mr.ctok[c], p);
+                    const float score = mix_child(L, K, p, c);
+                    const uint64_t key = tree_key(score, d, L.ctok[c], p);
                     if (key > s_tau) {
                         const int slot = atomicAdd(&s_ns, 1);
-                        M.skey[slot] = key;
-                        M.sinfo[slot] = (p << 16) | c;
+                        L.skey[slot] = key;
+                        L.sinfo[slot] = (p << 16) | c;
                     }
                 }
                 __syncthreads();
-                const int ns = s_ns;
+                const int nsc = s_ns;
                 // merge when the buffer could not take another chunk, at the
                 // end of the round, and while the list is not full
-                if (ns > 0 && (ns > kMixSurv - CH || base + CH >= total || nR < nmax)) {
-                    nR = mix_merge<NT>(Mr, K, nmax, nR, ns);
+                if (nsc > 0 && (nsc > kMixSurv - CH || base + CH >= total || nR < nmax)) {
+                    nR = mix_merge<NT>(L, K, nmax, nR, nsc, false, nullptr);
+                    swap_list(L);
                     if (tid == 0) {
                         s_ns = 0;
-                        s_tau = nR == nmax ? M.rkey[nmax - 1] : 0;
+                        s_tau = nR == nmax ? L.rkey[nmax - 1] : 0;
                     }
                     __syncthreads();
                 }
             }
         }
         __syncthreads();
-        if (np == 0) break;
     }
+    M.rkey = L.rkey;
     if (wv == 0) {
         mix_resolve(M, b, nmax, nR);
         ahat_fill(M.rho, M.ahat, nR);

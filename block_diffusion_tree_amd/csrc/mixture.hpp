@@ -34,8 +34,8 @@ constexpr int kMixSurv = 512;   // survivors buffered between merges
 constexpr int kMixMaxLds = 160 * 1024;   // LDS of one CU
 
 struct MixLayout {
-    int w, wq, prod, rowm, rows, chain, ids, first, ctok, cnt, qc, cq, cq2, rkey, rr, nkey, nr, ptab, skey,
-        sinfo, map, base, par, dep, tok, rho, ahat, total;
+    int w, wq, prod, rowm, rows, chain, ids, first, ctok, cnt, qc, cq, cq2, rkey, rr, nkey, nr, ptab, ptab2,
+        skey, sinfo, rankb, lob, map, base, par, dep, tok, rho, ahat, total;
 };
 
 __host__ __device__ inline int mix_align16(int x) { return (x + 15) & ~15; }
@@ -66,7 +66,7 @@ __host__ __device__ inline MixLayout mix_layout(int K, int b, int k, int nmax) {
     L.rho = o;   o = mix_align16(o + 4 * nn);
     L.ahat = o;  o = mix_align16(o + 8 * nn);
     // every position's q table, written by the gathers, read by the rounds
-    L.cq = o;    o = mix_align16(o + 4 * b * C * K);
+    L.cq = o;    o = mix_align16(o + 4 * b * C * K);   // [pos][z][c]
     L.cq2 = L.cq;
     // before the rounds
     int a = o;
@@ -80,23 +80,27 @@ __host__ __device__ inline MixLayout mix_layout(int K, int b, int k, int nmax) {
     L.nkey = r;  r = mix_align16(r + 8 * nmax);
     L.nr = r;    r = mix_align16(r + 4 * nmax * K);
     L.ptab = r;  r = mix_align16(r + 4 * nmax * K);
+    L.ptab2 = r; r = mix_align16(r + 4 * nmax * K);
     L.skey = r;  r = mix_align16(r + 8 * kMixSurv);
     L.sinfo = r; r = mix_align16(r + 4 * kMixSurv);
+    L.rankb = r; r = mix_align16(r + 4 * (nmax + kMixSurv));
+    L.lob = r;   r = mix_align16(r + 4 * (nmax + kMixSurv));
     L.total = a > r ? a : r;
     return L;
 }
 
 struct MixLds {
     double *w, *prod;
-    float *wq, *rowm, *rows, *cq, *rr, *nr, *ptab;
-    int32_t *chain, *ids, *first, *ctok, *cnt, *sinfo, *map, *base, *par, *dep, *tok;
+    float *wq, *rowm, *rows, *cq, *rr, *nr, *ptab, *ptab2;
+    int32_t *chain, *ids, *first, *ctok, *cnt, *sinfo, *rankb, *lob, *map, *base, *par, *dep, *tok;
     float *qc, *cq2;
     uint64_t *rkey, *nkey, *skey;
     float *rho;
     double *ahat;
+    int C;   // candidates per position: the stride of a cq row
 };
 
-__device__ __forceinline__ MixLds mix_lds(char *smem, const MixLayout &L) {
+__device__ __forceinline__ MixLds mix_lds(char *smem, const MixLayout &L, int C) {
     MixLds M;
     M.w = reinterpret_cast<double *>(smem + L.w);
     M.wq = reinterpret_cast<float *>(smem + L.wq);
@@ -116,6 +120,9 @@ __device__ __forceinline__ MixLds mix_lds(char *smem, const MixLayout &L) {
     M.nkey = reinterpret_cast<uint64_t *>(smem + L.nkey);
     M.nr = reinterpret_cast<float *>(smem + L.nr);
     M.ptab = reinterpret_cast<float *>(smem + L.ptab);
+    M.ptab2 = reinterpret_cast<float *>(smem + L.ptab2);
+    M.rankb = reinterpret_cast<int32_t *>(smem + L.rankb);
+    M.lob = reinterpret_cast<int32_t *>(smem + L.lob);
     M.skey = reinterpret_cast<uint64_t *>(smem + L.skey);
     M.sinfo = reinterpret_cast<int32_t *>(smem + L.sinfo);
     M.map = reinterpret_cast<int32_t *>(smem + L.map);
@@ -125,6 +132,7 @@ __device__ __forceinline__ MixLds mix_lds(char *smem, const MixLayout &L) {
     M.tok = reinterpret_cast<int32_t *>(smem + L.tok);
     M.rho = reinterpret_cast<float *>(smem + L.rho);
     M.ahat = reinterpret_cast<double *>(smem + L.ahat);
+    M.C = C;
     return M;
 }
 
@@ -134,66 +142,96 @@ __device__ __forceinline__ float mix_child(const MixLds &M, int K, int p, int c)
     float acc = 0.0f;
 #pragma unroll 8
     for (int z = 0; z < K; ++z)
-        acc = __builtin_fmaf(M.wq[z], __fmul_rn(M.ptab[p * K + z], M.cq[c * K + z]), acc);
+        acc = __builtin_fmaf(M.wq[z], __fmul_rn(M.ptab[p * K + z], M.cq[z * M.C + c]), acc);
     return acc;
 }
 
-// Merge the ns buffered survivors into the running list (nR sorted keys, at
-// most nmax): every element counts the larger keys; the count is its new
-// place.  Whole block.  Returns the new nR.
+// Merge the ns buffered survivors (all of the round's depth) into the
+// running list (nR sorted keys in M.rkey / M.rr, at most nmax).  An
+// element's new place is the number of larger keys: the list entries above
+// a survivor by binary search, the survivors above any element counted in
+// parts by several threads (M.rankb, zero on entry, is left zero).  The
+// merged list goes to M.nkey / M.nr; the caller swaps the buffers.  With
+// `parents`, the survivors that land also write their r values to M.ptab2
+// in list order (the parents of the next round: the landed survivors are
+// the largest ones, and a survivor's index among them is its place minus
+// the list entries above it) and their number to *np_next (zero on entry).
+// Whole block.  Returns the new list length.
 template <int THREADS>
-__device__ int mix_merge(const MixLds &M, int K, int nmax, int nR, int ns) {
+__device__ int mix_merge(const MixLds &M, int K, int nmax, int nR, int ns, bool parents, int *np_next) {
     const int tid = threadIdx.x;
     const int nE = nR + ns;
-    for (int e = tid; e < nE; e += THREADS) {
+    const int P = nE < THREADS ? THREADS / nE : 1;   // parts per element
+    const int per = (ns + P - 1) / P;
+    for (int t = tid; t < nE * P; t += THREADS) {
+        const int part = t / nE, e = t - part * nE;
         const uint64_t x = e < nR ? M.rkey[e] : M.skey[e - nR];
-        int rank;
-        if (e < nR) {
-            rank = e;
-        } else {
-            // larger keys of the sorted list: binary search
-            int lo = 0, hi = nR;
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (M.rkey[mid] > x) lo = mid + 1;
-                else hi = mid;
+        int cnt = 0;
+        if (part == 0) {
+            if (e < nR) {
+                cnt = e;
+            } else {
+                // larger keys of the sorted list: binary search
+                int lo = 0, hi = nR;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (M.rkey[mid] > x) lo = mid + 1;
+                    else hi = mid;
+                }
+                cnt = lo;
+                M.lob[e] = lo;
             }
-            rank = lo;
         }
-        // survivors above x: eight independent counts keep eight LDS reads
-        // in flight
+        // survivors above x in this part: eight independent counts keep
+        // eight LDS reads in flight
+        const int s0 = part * per, s1 = s0 + per < ns ? s0 + per : ns;
         int cnt8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        int s = 0;
-        for (; s + 8 <= ns; s += 8) {
+        int s = s0;
+        for (; s + 8 <= s1; s += 8) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) cnt8[u] += M.skey[s + u] > x ? 1 : 0;
         }
-        for (; s < ns; ++s) cnt8[0] += M.skey[s] > x ? 1 : 0;
+        for (; s < s1; ++s) cnt8[0] += M.skey[s] > x ? 1 : 0;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) rank += cnt8[u];
+        for (int u = 0; u < 8; ++u) cnt += cnt8[u];
+        atomicAdd(M.rankb + e, cnt);
+    }
+    __syncthreads();
+    for (int e = tid; e < nE; e += THREADS) {
+        const int rank = M.rankb[e];
+        M.rankb[e] = 0;
         if (rank < nmax) {
-            M.nkey[rank] = x;
             if (e < nR) {
+                M.nkey[rank] = M.rkey[e];
 #pragma unroll 8
                 for (int z = 0; z < K; ++z) M.nr[rank * K + z] = M.rr[e * K + z];
             } else {
+                M.nkey[rank] = M.skey[e - nR];
                 const int info = M.sinfo[e - nR];
                 const int p = info >> 16, c = info & 0xFFFF;
+                const int pi = rank - M.lob[e];
 #pragma unroll 8
-                for (int z = 0; z < K; ++z)
-                    M.nr[rank * K + z] = __fmul_rn(M.ptab[p * K + z], M.cq[c * K + z]);
+                for (int z = 0; z < K; ++z) {
+                    const float v = __fmul_rn(M.ptab[p * K + z], M.cq[z * M.C + c]);
+                    M.nr[rank * K + z] = v;
+                    if (parents) M.ptab2[pi * K + z] = v;
+                }
+                if (parents) atomicMax(np_next, pi + 1);
             }
         }
     }
     __syncthreads();
-    const int n = nE < nmax ? nE : nmax;
-    for (int i = tid; i < n; i += THREADS) {
-        M.rkey[i] = M.nkey[i];
-#pragma unroll 8
-        for (int z = 0; z < K; ++z) M.rr[i * K + z] = M.nr[i * K + z];
-    }
-    __syncthreads();
-    return n;
+    return nE < nmax ? nE : nmax;
+}
+
+// The merged list becomes the running one.
+__device__ __forceinline__ void swap_list(MixLds &L) {
+    uint64_t *tk = L.rkey;
+    L.rkey = L.nkey;
+    L.nkey = tk;
+    float *tr = L.rr;
+    L.rr = L.nr;
+    L.nr = tr;
 }
 
 __device__ __forceinline__ float mix_logit(const BuildParams &P, int64_t row, int token,
