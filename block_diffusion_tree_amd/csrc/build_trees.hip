@@ -277,53 +277,57 @@ __device__ SegmentResult stream_segment(const BuildParams &P, const char *row, i
 
     const int span = kThreads * U;
     const int n = v_hi - v_lo;
-    const int ntiles = n / span;
-    bool all[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) all[u] = true;
+    const int ntot = (n + span - 1) / span;   // tiles, the last one possibly partial
     const int vlo = v_lo;
+    // Every tile load is issued unconditionally: a lane past the segment's
+    // end reads the segment's last vector instead (the whole wave then reads
+    // one line) and its slot is masked to -inf before use.  A load under a
+    // condition would make the compiler's wait for a tile also wait for the
+    // loads issued after it, and the pair's second tile would then be
+    // processed with nothing in flight.
     u32x4 A[U], Bv[U];
-    auto fill = [&](u32x4 *dst, int t) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) dst[u] = load_vec<T>(rowv, vlo + t * span + u * kThreads + tid);
-    };
-    if (ntiles > 0) fill(A, 0);
-    int t = 0;
-    // The instruction arbiter favours older waves, so the blocks sharing a
-    // CU would otherwise finish one after another and leave the CU with a
-    // single streaming block at the end.  A wave's priority falls as its
-    // segment progresses, which keeps the co-resident blocks level.
-    int tier = -1;
-    for (; t + 1 < ntiles; t += 2) {
-        const int nt = (4 * t) / ntiles;
-        if (nt != tier) {
-            tier = nt;
-            if (nt == 0) __builtin_amdgcn_s_setprio(3);
-            else if (nt == 1) __builtin_amdgcn_s_setprio(2);
-            else if (nt == 2) __builtin_amdgcn_s_setprio(1);
-            else __builtin_amdgcn_s_setprio(0);
-        }
-        fill(Bv, t + 1);
-        st.tile(A, vlo + t * span, all, sm);
-        if (t + 2 < ntiles) fill(A, t + 2);
-        st.tile(Bv, vlo + (t + 1) * span, all, sm);
-    }
-    if (t < ntiles) st.tile(A, vlo + t * span, all, sm);
-    // ragged tile
-    {
-        bool ok[U];
-        bool anyv = false;
-        const int vb = vlo + ntiles * span;
+    bool okA[U], okB[U];
+    auto fill = [&](u32x4 *dst, bool *ok, int t) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int vi = vb + u * kThreads + tid;
+            const int vi = vlo + t * span + u * kThreads + tid;
             ok[u] = vi < v_hi;
-            anyv |= ok[u];
-            const u32x4 ninf = {Elem<T>::kNegInfWord, Elem<T>::kNegInfWord,
-                                Elem<T>::kNegInfWord, Elem<T>::kNegInfWord};
-            A[u] = ok[u] ? load_vec<T>(rowv, vi) : ninf;
+            dst[u] = load_vec<T>(rowv, ok[u] ? vi : v_hi - 1);
         }
-        if (__ballot(anyv)) st.tile(A, vb, ok, sm);
+    };
+    auto mask = [&](u32x4 *tl, const bool *ok, int t) {
+        if ((t + 1) * span <= n) return;   // full tile
+        const u32x4 ninf = {Elem<T>::kNegInfWord, Elem<T>::kNegInfWord, Elem<T>::kNegInfWord,
+                            Elem<T>::kNegInfWord};
+#pragma unroll
+        for (int u = 0; u < U; ++u) tl[u] = ok[u] ? tl[u] : ninf;
+    };
+    if (ntot > 0) {
+        fill(A, okA, 0);
+        // The instruction arbiter favours older waves, so the blocks sharing
+        // a CU would otherwise finish one after another and leave the CU
+        // with a single streaming block at the end.  A wave's priority falls
+        // as its segment progresses, which keeps the co-resident blocks
+        // level.
+        int tier = -1;
+        for (int t = 0; t < ntot; t += 2) {
+            const int nt = (4 * t) / ntot;
+            if (nt != tier) {
+                tier = nt;
+                if (nt == 0) __builtin_amdgcn_s_setprio(3);
+                else if (nt == 1) __builtin_amdgcn_s_setprio(2);
+                else if (nt == 2) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
+            }
+            fill(Bv, okB, t + 1);
+            mask(A, okA, t);
+            st.tile(A, vlo + t * span, okA, sm);
+            fill(A, okA, t + 2);
+            if (t + 1 < ntot) {
+                mask(Bv, okB, t + 1);
+                st.tile(Bv, vlo + (t + 1) * span, okB, sm);
+            }
+        }
     }
     // unaligned head and tail of the row (fewer than 2E elements), handled
     // by wave 0 of the last segment
