@@ -940,7 +940,7 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
     // the other buffers, which then become the current ones.
     MixLds L = M;
     int nR = 0;
-    int np = 1;               // round 1: the root
+    int np = 1;               // the first tree round has one parent: the root
     bool scan = false;        // parents to be found by a scan of the list
     __shared__ int s_npn;
     for (int i = tid; i < nmax + kMixSurv; i += NT) L.rankb[i] = 0;

@@ -34,7 +34,7 @@ constexpr int kMixSurv = 512;   // survivors buffered between merges
 constexpr int kMixMaxLds = 160 * 1024;   // LDS of one CU
 
 struct MixLayout {
-    int w, wq, prod, rowm, rows, chain, ids, first, ctok, cnt, qc, cq, cq2, rkey, rr, nkey, nr, ptab, ptab2,
+    int w, wq, prod, rowm, rows, chain, ids, first, ctok, cnt, qc, cq, rkey, rr, nkey, nr, ptab, ptab2,
         skey, sinfo, rankb, lob, map, base, par, dep, tok, rho, ahat, total;
 };
 
@@ -67,7 +67,6 @@ __host__ __device__ inline MixLayout mix_layout(int K, int b, int k, int nmax) {
     L.ahat = o;  o = mix_align16(o + 8 * nn);
     // every position's q table, written by the gathers, read by the rounds
     L.cq = o;    o = mix_align16(o + 4 * b * C * K);   // [pos][z][c]
-    L.cq2 = L.cq;
     // before the rounds
     int a = o;
     L.ids = a;   a = mix_align16(a + 4 * b * C);   // every position's top-k ids
@@ -93,7 +92,7 @@ struct MixLds {
     double *w, *prod;
     float *wq, *rowm, *rows, *cq, *rr, *nr, *ptab, *ptab2;
     int32_t *chain, *ids, *first, *ctok, *cnt, *sinfo, *rankb, *lob, *map, *base, *par, *dep, *tok;
-    float *qc, *cq2;
+    float *qc;
     uint64_t *rkey, *nkey, *skey;
     float *rho;
     double *ahat;
@@ -114,7 +113,6 @@ __device__ __forceinline__ MixLds mix_lds(char *smem, const MixLayout &L, int C)
     M.cnt = reinterpret_cast<int32_t *>(smem + L.cnt);
     M.qc = reinterpret_cast<float *>(smem + L.qc);
     M.cq = reinterpret_cast<float *>(smem + L.cq);
-    M.cq2 = reinterpret_cast<float *>(smem + L.cq2);
     M.rkey = reinterpret_cast<uint64_t *>(smem + L.rkey);
     M.rr = reinterpret_cast<float *>(smem + L.rr);
     M.nkey = reinterpret_cast<uint64_t *>(smem + L.nkey);
