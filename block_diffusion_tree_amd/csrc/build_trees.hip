@@ -220,8 +220,14 @@ struct Streamer {
                 }
             }
             wave_sync();
-            drain_stage();
         }
+    }
+
+    // Keys of the vectors a tile staged.  Called after the next tile's loads
+    // are out, so that two tiles stay in flight while it runs, and before the
+    // next tile stages (the stage holds one tile).
+    __device__ __forceinline__ void flush() {
+        if (nstage > 0) drain_stage();
     }
 };
 
@@ -320,14 +326,17 @@ __device__ SegmentResult stream_segment(const BuildParams &P, const char *row, i
                 else __builtin_amdgcn_s_setprio(0);
             }
             fill(Bv, okB, t + 1);
+            st.flush();   // the previous pair's second tile
             mask(A, okA, t);
             st.tile(A, vlo + t * span, okA, sm);
             fill(A, okA, t + 2);
+            st.flush();
             if (t + 1 < ntot) {
                 mask(Bv, okB, t + 1);
                 st.tile(Bv, vlo + (t + 1) * span, okB, sm);
             }
         }
+        st.flush();
     }
     // unaligned head and tail of the row (fewer than 2E elements), handled
     // by wave 0 of the last segment
