@@ -106,6 +106,30 @@ def test_trees_in_their_own_launch():
         assert torch.equal(g[f], g2[f]), f
 
 
+def test_sweep_full_workload_sampled_parity():
+    """The whole budget-sweep workload in one call, as the benchmark launches
+    it (4096 rows, trees in their own launch, online stop): rows of eight
+    queries against the reference's float64 softmax and top-k; every tree,
+    mask and position against the reference fed the GPU's own q."""
+    wl = synth.WORKLOADS["sweep"]
+    x = synth.make_logits(wl, device="cuda")
+    cost = cost_table(wl.B, wl.nmax, wl.seed, synth.LATENCY_A100)
+    g = binding.build_trees(x, k=wl.k, nmax=wl.nmax, nmin=1, cost=cost, l_ar=1.0)
+    torch.cuda.synchronize()
+    qs = [0, 1, 77, 128, 191, 200, 254, wl.B - 1]
+    sub = x[qs].cpu()
+    ref = oracle.softmax_topk(oracle.host_logits(sub), k=wl.k)
+    gsub = {f: g[f][qs] for f in ("topk_ids", "topk_q", "row_max", "row_sum")}
+    gc.check_rows(gsub, ref)
+    st = np.zeros((wl.B, wl.b), dtype=np.int32)   # every row of this input is finite
+    gc.check_tree(g, wl.b, wl.k, wl.nmax, 1, gc.np_(cost), 1.0, st)
+    gc.check_mask(g)
+    n = gc.np_(g["n_nodes"])
+    assert n.min() >= 1 and n.max() <= wl.nmax
+    del x
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("shape", [
     dict(B=4, b=16, V=30011, k=8, nmax=64),        # 16 waves per tree
     dict(B=3, b=3, V=4099, k=32, nmax=200),        # widest candidate lists
