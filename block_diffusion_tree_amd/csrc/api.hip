@@ -40,7 +40,6 @@ constexpr size_t kQueryTicketBase = kRowTicketWords;  // per-query counters
 constexpr size_t kTicketBytes = kTicketWords * 4;
 constexpr int kMaxSegments = 64;
 constexpr int64_t kResidentBlocks = 1024;   // stream blocks resident at once
-constexpr int kFewQueries = 4;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -173,9 +172,9 @@ int32_t bastion_build_trees(const void *logits, int32_t dtype, int32_t B, int32_
     P.row_ms = nullptr;
     // trees in a launch of their own (one block of 16 waves per query) when
     // the stream grid fills the machine more than once (256 CUs x 4 blocks),
-    // where a tree would hold a slot that later rows wait for, and when there
-    // are so few queries that no stream is left for the trees to overlap
-    P.split_trees = (rows * S > kResidentBlocks || B <= kFewQueries) ? 1 : 0;
+    // where a tree would hold a slot that later rows wait for; otherwise the
+    // whole call is one kernel
+    P.split_trees = rows * S > kResidentBlocks ? 1 : 0;
     {
         const char *env = getenv("BASTION_SPLIT_TREES");
         if (env) P.split_trees = atoi(env) != 0;
