@@ -596,9 +596,38 @@ __device__ void emit_tree(const BuildParams &P, int q, const int32_t *par, const
         P.qstatus[q] = status;
     }
     if (P.mask) {
-        // one thread per (node, mask word), each walking up from the node
         const int W = (W1 + 31) / 32;
         const int32_t pb = P.pos_base ? P.pos_base[q] : 0;
+        constexpr int kRegWords = 8;   // trees of up to 255 nodes
+        if (W <= kRegWords && W1 * W > NT) {
+            // more (node, word) pairs than threads: one thread per node, a
+            // single walk up from the node setting the bits of every word,
+            // held in registers
+            for (int i = tid; i < W1; i += NT) {
+                uint32_t bits[kRegWords];
+#pragma unroll
+                for (int w = 0; w < kRegWords; ++w) bits[w] = 0u;
+                int steps = 0;
+                if (i <= nstar) {
+                    int j = i;
+#pragma unroll
+                    for (int w = 0; w < kRegWords; ++w) bits[w] |= (j >> 5) == w ? 1u << (j & 31) : 0u;
+                    while (j > 0 && steps < b) {
+                        j = par[j];
+                        ++steps;
+#pragma unroll
+                        for (int w = 0; w < kRegWords; ++w)
+                            bits[w] |= (j >> 5) == w ? 1u << (j & 31) : 0u;
+                    }
+                }
+#pragma unroll
+                for (int w = 0; w < kRegWords; ++w)
+                    if (w < W) P.mask[(o + i) * W + w] = bits[w];
+                P.position_ids[o + i] = i <= nstar ? pb + steps : -1;
+            }
+            return;
+        }
+        // one thread per (node, mask word), each walking up from the node
         for (int e = tid; e < W1 * W; e += NT) {
             const int i = e / W, w = e - i * W;
             uint32_t bits = 0;
