@@ -314,10 +314,15 @@ __device__ SegmentResult stream_segment(const BuildParams &P, const char *row, i
         // a CU would otherwise finish one after another and leave the CU
         // with a single streaming block at the end.  A wave's priority falls
         // as its segment progresses, which keeps the co-resident blocks
-        // level.
+        // level; in a grid that is resident at once (at most four blocks per
+        // CU), blocks dispatched later (the grid is dispatched in order, over
+        // several microseconds) keep a higher priority for longer, by one
+        // tier per quarter of the grid.
+        const int age = gridDim.x <= 1024u ? int((blockIdx.x * 4u) / gridDim.x) : 0;
         int tier = -1;
         for (int t = 0; t < ntot; t += 2) {
-            const int nt = (4 * t) / ntot;
+            int nt = (4 * t) / ntot - age;
+            nt = nt < 0 ? 0 : nt;
             if (nt != tier) {
                 tier = nt;
                 if (nt == 0) __builtin_amdgcn_s_setprio(3);
