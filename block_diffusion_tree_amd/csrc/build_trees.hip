@@ -839,16 +839,21 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         const int z = c / k, j = c - z * k;
         M.ids[e] = ld_agent(P.topk_ids + (r0 + z * b + pos) * k + j);
     }
-    if (tid == 0) {
-        // prior weights, float64 softmax
-        double pm = -INFINITY, ps = 0.0;
-        for (int z = 0; z < K; ++z) pm = fmax(pm, double(P.prior[q * K + z]));
-        for (int z = 0; z < K; ++z) ps += exp(double(P.prior[q * K + z]) - pm);
-        for (int z = 0; z < K; ++z) {
-            const double w = exp(double(P.prior[q * K + z]) - pm) / ps;
-            M.w[z] = w;
-            M.wq[z] = float(w);
-            P.prior_q[q * K + z] = float(w);
+    if (wv == 0) {
+        // prior weights, float64 softmax: lane z forms exp(prior_z - max);
+        // the sum runs in branch order on every lane
+        const double pz = lane < K ? double(P.prior[q * K + lane]) : -INFINITY;
+        double pm = pz;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) pm = fmax(pm, __shfl_xor(pm, o));
+        const double ez = lane < K ? exp(pz - pm) : 0.0;
+        double ps = 0.0;
+        for (int z = 0; z < K; ++z) ps += __shfl(ez, z);
+        if (lane < K) {
+            const double w = ez / ps;
+            M.w[lane] = w;
+            M.wq[lane] = float(w);
+            P.prior_q[q * K + lane] = float(w);
         }
     }
     __syncthreads();
