@@ -146,14 +146,18 @@ def main():
     else:
         outs = [binding.alloc_tree_out(wl.B, wl.b, wl.k, wl.nmax, dev) for _ in range(nbuf)]
 
+    # one C call per step, its arguments marshalled once per input buffer (a
+    # caller looping over fixed buffers does the same), so that the host keeps
+    # ahead of the GPU and the events time the GPU work
+    if mixture:
+        calls = [binding.prepare_mixture_score(bufs[j], prior, k=wl.k, nmax=wl.nmax, out=mouts[j],
+                                               tree=outs[j], ws=ws)[2] for j in range(nbuf)]
+    else:
+        calls = [binding.prepare_build_trees(bufs[j], k=wl.k, nmax=wl.nmax, nmin=wl.nmin, cost=cost,
+                                             out=outs[j], ws=ws)[1] for j in range(nbuf)]
+
     def step(i):
-        j = i % nbuf
-        if mixture:
-            binding.mixture_score(bufs[j], prior, k=wl.k, nmax=wl.nmax, out=mouts[j], tree=outs[j],
-                                  ws=ws)
-        else:
-            binding.build_trees(bufs[j], k=wl.k, nmax=wl.nmax, nmin=wl.nmin, cost=cost,
-                                out=outs[j], ws=ws)
+        calls[i % nbuf]()
 
     for i in range(args.warmup):
         step(i)

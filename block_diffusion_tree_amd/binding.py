@@ -160,9 +160,9 @@ def _tree_struct(out):
     return TreeOut(*[(_ptr(out[n]) if n in out else None) for n, _ in TreeOut._fields_])
 
 
-def build_trees(logits, k: int, nmax: int, nmin: int = 1, cost=None, l_ar: float = 1.0,
-                pos_base=None, with_mask: bool = True, out=None, ws=None):
-    """bastion_build_trees on logits [B, b, V] (float32 or bfloat16, on GPU)."""
+def _build_trees_call(logits, k, nmax, nmin, cost, l_ar, pos_base, with_mask, out, ws):
+    """Checked arguments of one bastion_build_trees call: (out, call) where
+    call() makes the C call (the ctypes objects it needs stay alive with it)."""
     _dev(logits, "logits")
     if logits.dim() != 3 or logits.stride(2) != 1 or logits.stride(0) != logits.size(1) * logits.stride(1):
         raise ValueError("logits must be [B, b, V] with unit stride over V and rows packed")
@@ -182,11 +182,29 @@ def build_trees(logits, k: int, nmax: int, nmin: int = 1, cost=None, l_ar: float
     need = L.bastion_workspace_bytes(B, 1, b, V, k, nmax, dt)
     buf = w.get(need)
     st = _tree_struct(out)
-    _check(L.bastion_build_trees(_ptr(logits), dt, B, b, V, logits.stride(1), k, nmax, nmin,
-                                 cost_ptr, cstride, l_ar, _ptr(pos_base), C.byref(st),
-                                 _ptr(buf), buf.numel(), _stream()),
-           "bastion_build_trees")
+    args = (_ptr(logits), dt, B, b, V, logits.stride(1), k, nmax, nmin, cost_ptr, cstride, l_ar,
+            _ptr(pos_base), C.byref(st), _ptr(buf), buf.numel(), _stream())
+    fn = L.bastion_build_trees
+
+    def call(_keep=(st, buf, logits, cost, pos_base, out)):
+        _check(fn(*args), "bastion_build_trees")
+    return out, call
+
+
+def build_trees(logits, k: int, nmax: int, nmin: int = 1, cost=None, l_ar: float = 1.0,
+                pos_base=None, with_mask: bool = True, out=None, ws=None):
+    """bastion_build_trees on logits [B, b, V] (float32 or bfloat16, on GPU)."""
+    out, call = _build_trees_call(logits, k, nmax, nmin, cost, l_ar, pos_base, with_mask, out, ws)
+    call()
     return out
+
+
+def prepare_build_trees(logits, k: int, nmax: int, nmin: int = 1, cost=None, l_ar: float = 1.0,
+                        pos_base=None, with_mask: bool = True, out=None, ws=None):
+    """The same call with its arguments checked and marshalled once, on the
+    current stream: returns (out, call), and every call() repeats it on the
+    same tensors (what a caller that loops over fixed buffers does)."""
+    return _build_trees_call(logits, k, nmax, nmin, cost, l_ar, pos_base, with_mask, out, ws)
 
 
 def budget_select(ahat, n_avail, nmin: int, cost, l_ar: float = 1.0, with_curve: bool = True):
@@ -236,11 +254,7 @@ def alloc_mixture_out(B, K, b, k, device):
                 row_sum=torch.empty((B, K, b), **f32))
 
 
-def mixture_score(branch_logits, prior_logits, k: int, nmax: int, with_tree: bool = True,
-                  with_mask: bool = True, out=None, tree=None, ws=None):
-    """bastion_mixture_score on branch logits [B, K, b, V] (float32 or bfloat16)
-    and prior logits [B, K] float32, on GPU.  Returns (mixture outputs, tree
-    outputs or None)."""
+def _mixture_call(branch_logits, prior_logits, k, nmax, with_tree, with_mask, out, tree, ws):
     _dev(branch_logits, "branch_logits")
     _dev(prior_logits, "prior_logits")
     x = branch_logits
@@ -261,8 +275,30 @@ def mixture_score(branch_logits, prior_logits, k: int, nmax: int, with_tree: boo
     w = _workspace(ws, x.device)
     buf = w.get(L.bastion_workspace_bytes(B, K, b, V, k, nmax, dt))
     mo = MixOut(*[_ptr(out[n]) for n, _ in MixOut._fields_])
-    ts = None if tree is None else C.byref(_tree_struct(tree))
-    _check(L.bastion_mixture_score(_ptr(x), dt, _ptr(prior_logits), B, K, b, V, x.stride(2), k,
-                                   nmax, C.byref(mo), ts, _ptr(buf), buf.numel(), _stream()),
-           "bastion_mixture_score")
+    tst = None if tree is None else _tree_struct(tree)
+    ts = None if tst is None else C.byref(tst)
+    args = (_ptr(x), dt, _ptr(prior_logits), B, K, b, V, x.stride(2), k, nmax, C.byref(mo), ts,
+            _ptr(buf), buf.numel(), _stream())
+    fn = L.bastion_mixture_score
+
+    def call(_keep=(mo, tst, buf, x, prior_logits, out, tree)):
+        _check(fn(*args), "bastion_mixture_score")
+    return out, tree, call
+
+
+def mixture_score(branch_logits, prior_logits, k: int, nmax: int, with_tree: bool = True,
+                  with_mask: bool = True, out=None, tree=None, ws=None):
+    """bastion_mixture_score on branch logits [B, K, b, V] (float32 or bfloat16)
+    and prior logits [B, K] float32, on GPU.  Returns (mixture outputs, tree
+    outputs or None)."""
+    out, tree, call = _mixture_call(branch_logits, prior_logits, k, nmax, with_tree, with_mask,
+                                    out, tree, ws)
+    call()
     return out, tree
+
+
+def prepare_mixture_score(branch_logits, prior_logits, k: int, nmax: int, with_tree: bool = True,
+                          with_mask: bool = True, out=None, tree=None, ws=None):
+    """mixture_score with its arguments checked and marshalled once: returns
+    (out, tree, call)."""
+    return _mixture_call(branch_logits, prior_logits, k, nmax, with_tree, with_mask, out, tree, ws)
