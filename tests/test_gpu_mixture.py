@@ -123,3 +123,15 @@ def test_many_ties_across_branches():
     x = torch.randint(-3, 4, (3, 4, 6, 257)).float().to("cuda")
     prior = torch.randint(-1, 2, (3, 4)).float().to("cuda")
     check_mixture(x, prior, 5, 50)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=4, K=8, b=5, V=3000, k=12, nmax=40),     # unions of up to 96 ids
+    dict(B=2, K=16, b=2, V=5000, k=20, nmax=30),    # unions of up to 320 ids
+])
+def test_wide_unions_full_parity(shape):
+    """Unions wider than one wave (the first-occurrence and rank path)."""
+    wl = synth.scaled(synth.WORKLOADS["mixture"], dtype="f32", **shape)
+    x = synth.make_logits(wl, seed=12).to("cuda")
+    prior = synth.make_prior_logits(wl).to("cuda")
+    check_mixture(x, prior, wl.k, wl.nmax)
