@@ -322,3 +322,18 @@ def test_malformed_tree_mask_matches_reference():
     torch.cuda.synchronize()
     rm, rp = oracle.tree_mask(gc.np_(parent), gc.np_(n))
     assert (gc.np_(mask).view(np.uint32) == rm).all() and (gc.np_(pos) == rp).all()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_largest_vocabulary(dtype):
+    """V = 2^19, the largest the 19-bit token field of the pop keys holds, with
+    the leaders among the last token ids (and ties between them in bf16)."""
+    V = 1 << 19
+    g = torch.Generator().manual_seed(21)
+    x = torch.randn(2, 3, V, generator=g) * 2.0
+    for q in range(2):
+        for p in range(3):
+            x[q, p, V - 1 - (q + p)] = 9.0
+            x[q, p, V - 5 - p] = 8.5
+            x[q, p, V - 9] = 8.5
+    gc.run_and_check(x.to(dtype).to("cuda"), 6, 30)
