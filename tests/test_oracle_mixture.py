@@ -157,3 +157,99 @@ def test_full_mixture_tree_mass(oracle_mod):
     assert t["n_nodes"].tolist() == [full, full]
     assert np.allclose(t["ahat"][:, full], 1.0 + b, rtol=1e-5)
     assert (np.diff(t["rho"][:, 1:], axis=1) <= 0).all()
+
+
+def test_qdep_one_hot_disjoint_branches(oracle_mod):
+    """Branches that put all their mass on one token per position, on tokens
+    no other branch uses (every other entry -inf): chain z gets probability 1
+    from branch z and 0 from every other branch, so its q_dep is exactly the
+    prior weight w_z (DBlast page, Methodology 1, the latent-mixture
+    q_dep).  Holds for several K and b with an unequal prior."""
+    for K, b in ((2, 2), (3, 4), (4, 3)):
+        V = K * b + 5
+        B = 2
+        x = np.full((B, K, b, V), -np.inf, np.float32)
+        for qq in range(B):
+            for z in range(K):
+                for i in range(b):
+                    x[qq, z, i, (z * b + i + qq) % V] = 1.5 + z
+        prior = np.array([[0.7 * z - 0.4 * z * z + qq for z in range(K)] for qq in range(B)],
+                         np.float32)
+        m = oracle_mod.mixture(x, prior, k=1)
+        for qq in range(B):
+            e = np.exp(prior[qq].astype(np.float64) - prior[qq].max())
+            w = e / e.sum()
+            assert len(set(np.round(w, 12))) == K   # the prior is unequal
+            for z in range(K):
+                assert m["chain_tokens"][qq, z].tolist() == [(z * b + i + qq) % V
+                                                            for i in range(b)]
+                assert m["qdep_chain"][qq, z] == pytest.approx(w[z], rel=1e-14)
+
+
+def test_qdep_two_branches_by_hand(oracle_mod):
+    """K = 2, b = 2, V = 2 with logits ln(n) chosen so that every probability
+    is a small fraction (two-entry softmax = sigmoid of the difference):
+
+      branch 0: position 0 p = (1/4, 3/4), position 1 p = (2/3, 1/3) -> chain (1, 0)
+      branch 1: position 0 p = (4/5, 1/5), position 1 p = (1/10, 9/10) -> chain (0, 1)
+      prior weights (1/4, 3/4)
+
+    q_dep(chain 0) = 1/4 * 3/4 * 2/3 + 3/4 * 1/5 * 1/10 = 0.14 and
+    q_dep(chain 1) = 1/4 * 1/4 * 1/3 + 3/4 * 4/5 * 9/10 = 0.5608333...
+    Scoring a chain on its own branch only would give 0.5 and 0.72; swapping
+    the chain and branch indices 0.1875 and 0.44."""
+    ln = np.log
+    x = np.array([[[[0.0, ln(3)], [ln(2), 0.0]],
+                   [[ln(4), 0.0], [0.0, ln(9)]]]], np.float32)
+    prior = np.array([[0.0, ln(3)]], np.float32)
+    m = oracle_mod.mixture(x, prior, k=1)
+    assert m["chain_tokens"][0].tolist() == [[1, 0], [0, 1]]
+    expect = [1 / 4 * 3 / 4 * 2 / 3 + 3 / 4 * 1 / 5 * 1 / 10,
+              1 / 4 * 1 / 4 * 1 / 3 + 3 / 4 * 4 / 5 * 9 / 10]
+    # float32 rounding of ln(n) moves each probability by < 1e-7 relative
+    assert m["qdep_chain"][0].tolist() == pytest.approx(expect, rel=1e-6)
+    # the same sequences scored by the sequence routine
+    qs = oracle_mod.qdep_sequences(x, prior, m["chain_tokens"])
+    assert qs[0].tolist() == pytest.approx(expect, rel=1e-6)
+
+
+def test_qdep_sequences_by_hand(oracle_mod):
+    """The sequence routine on every sequence of the hand example above,
+    each written out as w_0 p_0(s) + w_1 p_1(s)."""
+    ln = np.log
+    x = np.array([[[[0.0, ln(3)], [ln(2), 0.0]],
+                   [[ln(4), 0.0], [0.0, ln(9)]]]], np.float32)
+    prior = np.array([[0.0, ln(3)]], np.float32)
+    p = {0: [[1 / 4, 3 / 4], [2 / 3, 1 / 3]], 1: [[4 / 5, 1 / 5], [1 / 10, 9 / 10]]}
+    w = [1 / 4, 3 / 4]
+    seqs = np.array([[[0, 0], [0, 1], [1, 0], [1, 1]]], np.int32)
+    got = oracle_mod.qdep_sequences(x, prior, seqs)[0]
+    for s, (a, c) in enumerate(seqs[0].tolist()):
+        want = w[0] * p[0][0][a] * p[0][1][c] + w[1] * p[1][0][a] * p[1][1][c]
+        assert got[s] == pytest.approx(want, rel=1e-6)
+    assert got.sum() == pytest.approx(1.0, abs=1e-14)
+
+
+def test_qdep_random_branches_match_sequence_routine(oracle_mod):
+    """Distinct random branches (K = 3, b = 3): the chain scores equal the
+    sequence routine run on the chains, and a brute-force double sum over
+    the float64 softmax of every row."""
+    rng = np.random.default_rng(11)
+    B, K, b, V = 2, 3, 3, 7
+    x = rand_branch_logits(rng, B, K, b, V, scale=1.5)
+    prior = np.array([[0.3, -1.1, 0.9], [2.0, 0.0, -0.5]], np.float32)
+    m = oracle_mod.mixture(x, prior, k=2)
+    qs = oracle_mod.qdep_sequences(x, prior, m["chain_tokens"])
+    assert np.allclose(m["qdep_chain"], qs, rtol=1e-14, atol=0)
+    xd = x.astype(np.float64)
+    p = np.exp(xd - xd.max(axis=-1, keepdims=True))
+    p /= p.sum(axis=-1, keepdims=True)
+    for qq in range(B):
+        w = np.exp(prior[qq].astype(np.float64) - prior[qq].max())
+        w /= w.sum()
+        for z in range(K):
+            chain = m["chain_tokens"][qq, z]
+            assert chain.tolist() == [int(np.argmax(x[qq, z, i])) for i in range(b)]
+            want = sum(w[zp] * np.prod([p[qq, zp, i, chain[i]] for i in range(b)])
+                       for zp in range(K))
+            assert m["qdep_chain"][qq, z] == pytest.approx(want, rel=1e-12)
