@@ -59,9 +59,6 @@
 #define ORACLE_BAD_LOGITS 1
 #define ORACLE_EXHAUSTED 2
 
-/* A row whose maximum has magnitude above 2^20 is rejected as bad input. */
-#define ORACLE_MAX_ABS_ROW_MAX 1048576.0
-
 int oracle_abi_version(void) { return 1; }
 
 #ifdef _OPENMP
@@ -89,8 +86,8 @@ static double logit_at(const void *base, int dtype, int64_t idx)
  * For each row: M = max_v l_v, S = sum_v exp(l_v - M),
  * p(v) = exp(l_v - M) / S, and the k tokens ranked first by
  * (logit desc, id asc), each with its p.
- * A row is bad when it holds a NaN or +inf, when every entry is -inf, or
- * when |M| exceeds 2^20.
+ * A row is bad when it holds a NaN or +inf, or when every entry is -inf;
+ * any other row (however large its logits) gets its softmax.
  * ------------------------------------------------------------------------ */
 void oracle_softmax_topk(const void *logits, int dtype, int64_t nrows, int V,
                          int64_t row_stride, int k, double *row_max,
@@ -110,7 +107,7 @@ void oracle_softmax_topk(const void *logits, int dtype, int64_t nrows, int V,
             else if (x[v] > M)
                 M = x[v];
         }
-        if (M == -INFINITY || fabs(M) > ORACLE_MAX_ABS_ROW_MAX)
+        if (M == -INFINITY)
             bad = 1;
         row_status[r] = bad ? ORACLE_BAD_LOGITS : ORACLE_OK;
         if (bad) {

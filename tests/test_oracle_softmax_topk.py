@@ -95,17 +95,30 @@ def test_bf16_decode(oracle_mod):
     assert r["row_sum"][0] == pytest.approx(S, rel=1e-15)
 
 
-@pytest.mark.parametrize("bad", ["nan", "posinf", "allneginf", "huge"])
+@pytest.mark.parametrize("bad", ["nan", "posinf", "allneginf"])
 def test_bad_rows(oracle_mod, bad):
     x = np.zeros((2, 16), np.float32)
     if bad == "nan":
         x[1, 3] = np.nan
     elif bad == "posinf":
         x[1, 3] = np.inf
-    elif bad == "allneginf":
-        x[1, :] = -np.inf
     else:
-        x[1, 5] = 2.0 ** 21
+        x[1, :] = -np.inf
     r = oracle_mod.softmax_topk(x, k=2)
     assert r["row_status"].tolist() == [0, 1]
     assert r["topk_ids"][1].tolist() == [-1, -1]
+
+
+def test_large_logits_are_a_plain_softmax(oracle_mod):
+    """Logits far from zero are valid input: the softmax only sees
+    differences, so integer logits shifted by 2^21 or 2^23 (exact in float32)
+    give the same ids and probabilities as the unshifted row."""
+    rng = np.random.default_rng(9)
+    y = rng.integers(-6, 7, size=(4, 50)).astype(np.float32)
+    a = oracle_mod.softmax_topk(y, k=6)
+    for shift in (2.0 ** 21, -(2.0 ** 21), 2.0 ** 23):
+        r = oracle_mod.softmax_topk(y + np.float32(shift), k=6)
+        assert (r["row_status"] == 0).all()
+        assert (r["topk_ids"] == a["topk_ids"]).all()
+        assert np.allclose(r["topk_p"], a["topk_p"], rtol=1e-13, atol=0)
+        assert np.allclose(r["row_sum"], a["row_sum"], rtol=1e-13, atol=0)
