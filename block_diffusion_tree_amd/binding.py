@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbastion.so")
 
 OK, EINVAL, EUNSUPPORTED, EHIP, EWORKSPACE = 0, 1, 2, 3, 4
-Q_OK, Q_BAD_LOGITS, Q_EXHAUSTED = 0, 1, 2
+Q_OK, Q_BAD_LOGITS, Q_EXHAUSTED, Q_RANGE = 0, 1, 2, 3
 F32, BF16 = 0, 1
 
 _lib = None

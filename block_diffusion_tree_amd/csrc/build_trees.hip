@@ -721,9 +721,11 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
             S.cost[e] = P.cost[int64_t(q) * P.cost_qstride + e];
     if (tid == 0) s_bad = 0;
     __syncthreads();
-    if (rst != BASTION_Q_OK) atomicOr(&s_bad, 1);
+    if (rst != BASTION_Q_OK) atomicOr(&s_bad, rst == BASTION_Q_RANGE ? 2 : 1);
     __syncthreads();
     const bool bad = s_bad != 0;
+    // a bad row outranks a row outside the float32 range
+    const int bad_status = (s_bad & 1) ? BASTION_Q_BAD_LOGITS : BASTION_Q_RANGE;
 
     __shared__ int s_pool;
     int cnt = -1;
@@ -810,7 +812,7 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
     }
     __syncthreads();
     const int nstar = bad ? 0 : s_nstar;
-    const int status = bad ? BASTION_Q_BAD_LOGITS : s_status;
+    const int status = bad ? bad_status : s_status;
     emit_tree<NT>(P, q, S.par, S.dep, S.tok, S.rho, S.ahat, nstar, bad, status);
 }
 
@@ -832,7 +834,8 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
     for (int e = tid; e < K * b; e += NT) {
         M.rowm[e] = ld_agent(P.row_ms + 2 * (r0 + e));
         M.rows[e] = ld_agent(P.row_ms + 2 * (r0 + e) + 1);
-        if (ld_agent(P.row_status + r0 + e) != BASTION_Q_OK) atomicOr(&s_bad, 1);
+        const int32_t rst = ld_agent(P.row_status + r0 + e);
+        if (rst != BASTION_Q_OK) atomicOr(&s_bad, rst == BASTION_Q_RANGE ? 2 : 1);
     }
     for (int e = tid; e < b * C; e += NT) {
         const int pos = e / C, c = e - pos * C;
@@ -865,7 +868,9 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         for (int e = tid; e < b * C; e += NT) P.cand_tokens[cbase + e] = -1;
         for (int e = tid; e < b * C * K; e += NT) P.cand_q[cbase * K + e] = 0.0f;
         for (int i = tid; i < b; i += NT) P.cand_count[int64_t(q) * b + i] = 0;
-        if (P.mix_tree) emit_tree<NT>(P, q, M.par, M.dep, M.tok, M.rho, M.ahat, 0, true, BASTION_Q_BAD_LOGITS);
+        if (P.mix_tree)
+            emit_tree<NT>(P, q, M.par, M.dep, M.tok, M.rho, M.ahat, 0, true,
+                          (s_bad & 1) ? BASTION_Q_BAD_LOGITS : BASTION_Q_RANGE);
         return;
     }
     // chains: the top-1 token of every branch row (chain[z * b + i])
@@ -1197,7 +1202,11 @@ __global__ __launch_bounds__(kThreads, (R >= 16 ? 2 : 4)) void build_trees_kerne
     }
     // ---- finish the row (wave 0) ----
     if (wv == 0) {
-        const bool badrow = (nsel < P.k) || !(Ssum == Ssum) || !(fabsf(M) <= kMaxAbsRowMax);
+        // a NaN or +inf entry, or a row of -inf only, is bad input; a finite
+        // row max beyond 2^20 is outside the library's float32 range
+        const bool invalid = (nsel < P.k) || !(Ssum == Ssum) || !(fabsf(M) <= 3.402823466e38f);
+        const bool badrow = invalid || !(fabsf(M) <= kMaxAbsRowMax);
+        const int32_t rowst = invalid ? BASTION_Q_BAD_LOGITS : BASTION_Q_RANGE;
         const int64_t o = int64_t(row) * P.k;
         if (lane < P.k) {
             if (badrow) {
@@ -1216,7 +1225,7 @@ __global__ __launch_bounds__(kThreads, (R >= 16 ? 2 : 4)) void build_trees_kerne
             const float d = __builtin_fmaf(M, kLog2e, -C);   // rounding residual of C
             P.row_max[row] = badrow ? 0.0f : M;
             P.row_sum[row] = badrow ? 0.0f : Ssum * __builtin_amdgcn_exp2f(-d);
-            st_agent(P.row_status + row, int32_t(badrow ? BASTION_Q_BAD_LOGITS : BASTION_Q_OK));
+            st_agent(P.row_status + row, badrow ? rowst : int32_t(BASTION_Q_OK));
             if (P.row_ms) {
                 st_agent(P.row_ms + 2 * row, M);
                 st_agent(P.row_ms + 2 * row + 1, Ssum);

@@ -65,10 +65,16 @@ extern "C" {
 
 /* per-query status */
 #define BASTION_Q_OK 0
-#define BASTION_Q_BAD_LOGITS 1  /* a row holds NaN or +inf, is all -inf, or
-                                   |row max| > 2^20: the tree is the root alone */
+#define BASTION_Q_BAD_LOGITS 1  /* a row holds NaN or +inf, or is all -inf:
+                                   the tree is the root alone */
 #define BASTION_Q_EXHAUSTED 2   /* informational: the candidate tree had
                                    fewer nodes than the budget asked for */
+#define BASTION_Q_RANGE 3       /* library limit, not a property of the
+                                   method: a row's maximum logit has magnitude
+                                   above 2^20, where the float32 softmax is
+                                   not guaranteed to 1e-5; the row is refused
+                                   like a bad one (the tree is the root alone)
+                                   and BASTION_Q_BAD_LOGITS takes precedence */
 
 /* logits storage types */
 #define BASTION_F32 0

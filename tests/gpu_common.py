@@ -23,9 +23,23 @@ def np_(t):
     return t.detach().cpu().numpy()
 
 
-def check_rows(g, ref, rows_ok=None):
+# The library refuses rows whose maximum logit exceeds 2^20 in magnitude
+# (BASTION_Q_RANGE, a float32 range limit of the library, not of the method);
+# the reference computes their softmax.  Such rows are expected refused.
+RANGE_LIMIT = 2.0 ** 20
+
+
+def expected_row_status(ref):
+    """The reference's row status with the library's range limit applied."""
+    st = np.array(ref["row_status"], copy=True)
+    big = (st == oracle.OK) & (np.abs(ref["row_max"]) > RANGE_LIMIT)
+    st[big] = binding.Q_RANGE
+    return st
+
+
+def check_rows(g, ref):
     """GPU row outputs vs the reference's float64 softmax/top-k."""
-    st = ref["row_status"].reshape(-1)
+    st = expected_row_status(ref).reshape(-1)
     gi = np_(g["topk_ids"]).reshape(st.size, -1)
     gq = np_(g["topk_q"]).reshape(st.size, -1)
     good = st == oracle.OK
@@ -48,6 +62,11 @@ def check_tree(g, wl_b, k, nmax, nmin=1, cost=None, l_ar=1.0, row_status=None):
     q = np_(g["topk_q"])
     ref = oracle.best_first(ids, q, nmax=nmax, nmin=nmin, cost=cost, l_ar=l_ar,
                             row_status=row_status)
+    if row_status is not None:
+        # queries refused only for the range limit report BASTION_Q_RANGE
+        rs = np.asarray(row_status).reshape(ids.shape[0], -1)
+        only_range = (rs == binding.Q_RANGE).any(axis=1) & ~(rs == oracle.BAD_LOGITS).any(axis=1)
+        ref["qstatus"][only_range] = binding.Q_RANGE
     for f in ("n_nodes", "qstatus", "parent", "depth", "token"):
         a, r = np_(g[f]), ref[f]
         assert (a == r).all(), f"{f} differs at {np.argwhere(a != r)[:5].tolist()}"
@@ -73,7 +92,7 @@ def run_and_check(logits, k, nmax, nmin=1, cost=None, l_ar=1.0, pos_base=None, r
         ref_rows = oracle.softmax_topk(oracle.host_logits(logits), k=k)
     check_rows(g, ref_rows)
     cost_h = None if cost is None else np_(cost)
-    check_tree(g, logits.shape[1], k, nmax, nmin, cost_h, l_ar, ref_rows["row_status"])
+    check_tree(g, logits.shape[1], k, nmax, nmin, cost_h, l_ar, expected_row_status(ref_rows))
     check_mask(g, pos_base)
     return g, ref_rows
 

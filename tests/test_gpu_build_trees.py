@@ -157,10 +157,13 @@ def test_bad_rows_and_padding():
     x[0, 1, 17] = float("nan")
     x[1, 2, 5] = float("inf")
     x[2, 0, :] = float("-inf")
-    x[3, 1, 9] = 2.0 ** 21
+    x[3, 1, 9] = 2.0 ** 21     # valid, but beyond the library's float32 range
+    x[4, 2, 0] = -(2.0 ** 20)  # a large negative logit in an ordinary row
     g, ref = gc.run_and_check(x.to("cuda"), wl.k, wl.nmax)
-    assert gc.np_(g["qstatus"]).tolist() == [1, 1, 1, 1, 0]
+    assert ref["row_status"][3, 1] == oracle.OK
+    assert gc.np_(g["qstatus"]).tolist() == [1, 1, 1, binding.Q_RANGE, 0]
     assert gc.np_(g["n_nodes"]).tolist()[:4] == [0, 0, 0, 0]
+    assert int(gc.np_(g["n_nodes"])[4]) == wl.nmax
 
 
 def test_one_hot_rows_give_a_chain_then_zero_mass():
