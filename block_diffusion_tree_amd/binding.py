@@ -68,6 +68,8 @@ def lib():
         L.bastion_tree_mask.argtypes = [P, P, I32, I32, P, P, P, P]
         L.bastion_accept.restype = I32
         L.bastion_accept.argtypes = [P, P, P, I32, I32, I32, P, P, P, P, P]
+        L.bastion_set_tuning.restype = None
+        L.bastion_set_tuning.argtypes = [I32, I32]
         L.bastion_mixture_score.restype = I32
         L.bastion_mixture_score.argtypes = [P, I32, P, I32, I32, I32, I32, I64, I32, I32,
                                             C.POINTER(MixOut), C.POINTER(TreeOut), P, SZ, P]
@@ -110,18 +112,31 @@ def _dtype_code(t):
 
 
 class Workspace:
-    """Device scratch for the fused calls (grows on demand, zeroed once)."""
+    """Device scratch for the fused calls (grows on demand, zeroed once).
+
+    Calls that share a workspace must not overlap in time: its arrival
+    counters belong to one call at a time.  A workspace used on a stream
+    other than the one it was allocated on is recorded on that stream, so
+    that torch does not hand its memory to someone else while such a call
+    may still run (when it grows, or when it is dropped)."""
 
     def __init__(self, device=None):
         self.device = device
         self.buf = None
+        self._alloc_stream = None
 
     def get(self, nbytes: int):
+        cur = torch.cuda.current_stream(self.device)
         if self.buf is None or self.buf.numel() < nbytes:
+            old = self.buf
             self.buf = torch.empty(max(nbytes, 1 << 18), dtype=torch.uint8,
                                    device=self.device or "cuda")
+            self._alloc_stream = cur
             _check(lib().bastion_workspace_init(_ptr(self.buf), self.buf.numel(), _stream()),
                    "bastion_workspace_init")
+            del old   # recorded on every other stream that used it
+        elif cur != self._alloc_stream:
+            self.buf.record_stream(cur)
         return self.buf
 
 
@@ -129,12 +144,54 @@ _default_ws = {}
 
 
 def _workspace(ws, device):
+    """The caller's workspace, else one per (device, stream): calls on
+    different streams never share arrival counters."""
     if ws is not None:
         return ws
-    key = str(device)
+    stream = torch.cuda.current_stream(device)
+    key = (str(device), stream.cuda_stream)
     if key not in _default_ws:
         _default_ws[key] = Workspace(device)
     return _default_ws[key]
+
+
+def set_tuning(segments: int = 0, split_trees: int = -1):
+    """bastion_set_tuning: launch-plan overrides (0 / -1: the library's plan)."""
+    lib().bastion_set_tuning(int(segments), int(split_trees))
+
+
+def _need(t, name, dtype, shape=None, device=None):
+    """t must be a contiguous GPU tensor of `dtype` (and `shape`, `device`)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    return t
+
+
+def _cost_stride(cost, B, nmax, device):
+    """Checks a cost table [1 or B, >= nmax+1] (or [>= nmax+1]) float64 and
+    returns its per-query stride (0 when shared)."""
+    if cost.dim() == 1:
+        rows, cols = 1, cost.size(0)
+    elif cost.dim() == 2:
+        rows, cols = cost.size(0), cost.size(1)
+    else:
+        raise ValueError("cost must be [nmax+1], [1, nmax+1] or [B, nmax+1]")
+    if cols < nmax + 1:
+        raise ValueError(f"cost needs at least nmax+1 = {nmax + 1} columns, got {cols}")
+    if rows not in (1, B):
+        raise ValueError(f"cost needs 1 or B = {B} rows, got {rows}")
+    _need(cost, "cost", torch.float64, device=device)
+    return 0 if rows == 1 else cols
 
 
 def alloc_tree_out(B, b, k, nmax, device, with_rows=True, with_mask=True):
@@ -156,6 +213,25 @@ def alloc_tree_out(B, b, k, nmax, device, with_rows=True, with_mask=True):
     return out
 
 
+def _check_tree_out(out, B, b, k, nmax, device, with_rows):
+    """Caller-supplied outputs must have the shapes and types the call writes."""
+    W1 = nmax + 1
+    W = (W1 + 31) // 32
+    i32, f32, f64 = torch.int32, torch.float32, torch.float64
+    spec = dict(parent=(i32, (B, W1)), depth=(i32, (B, W1)), token=(i32, (B, W1)),
+                rho=(f32, (B, W1)), ahat=(f64, (B, W1)), n_nodes=(i32, (B,)),
+                qstatus=(i32, (B,)))
+    if with_rows:
+        spec.update(topk_ids=(i32, (B, b, k)), topk_q=(f32, (B, b, k)), row_max=(f32, (B, b)),
+                    row_sum=(f32, (B, b)))
+    if "mask" in out:
+        spec.update(mask=(i32, (B, W1, W)), position_ids=(i32, (B, W1)))
+    for name, (dt, shape) in spec.items():
+        if name not in out:
+            raise ValueError(f"output {name!r} is missing")
+        _need(out[name], name, dt, shape, device)
+
+
 def _tree_struct(out):
     return TreeOut(*[(_ptr(out[n]) if n in out else None) for n, _ in TreeOut._fields_])
 
@@ -172,11 +248,11 @@ def _build_trees_call(logits, k, nmax, nmin, cost, l_ar, pos_base, with_mask, ou
         out = alloc_tree_out(B, b, k, nmax, logits.device, with_mask=with_mask)
     cost_ptr, cstride = None, 0
     if cost is not None:
-        _dev(cost, "cost")
-        if cost.dtype != torch.float64 or not cost.is_contiguous():
-            raise TypeError("cost must be a contiguous float64 GPU tensor")
-        cstride = 0 if cost.dim() == 1 or cost.size(0) == 1 else cost.size(1)
+        cstride = _cost_stride(cost, B, nmax, logits.device)
         cost_ptr = _ptr(cost)
+    if pos_base is not None:
+        _need(pos_base, "pos_base", torch.int32, (B,), logits.device)
+    _check_tree_out(out, B, b, k, nmax, logits.device, with_rows=True)
     L = lib()
     w = _workspace(ws, logits.device)
     need = L.bastion_workspace_bytes(B, 1, b, V, k, nmax, dt)
@@ -208,10 +284,14 @@ def prepare_build_trees(logits, k: int, nmax: int, nmin: int = 1, cost=None, l_a
 
 
 def budget_select(ahat, n_avail, nmin: int, cost, l_ar: float = 1.0, with_curve: bool = True):
+    if ahat.dim() != 2:
+        raise ValueError("ahat must be [B, nmax+1]")
     B, W1 = ahat.shape
+    _need(ahat, "ahat", torch.float64)
+    _need(n_avail, "n_avail", torch.int32, (B,), ahat.device)
+    cstride = _cost_stride(cost, B, W1 - 1, ahat.device)
     nstar = torch.empty((B,), dtype=torch.int32, device=ahat.device)
     s = torch.empty((B, W1), dtype=torch.float64, device=ahat.device) if with_curve else None
-    cstride = 0 if cost.dim() == 1 or cost.size(0) == 1 else cost.size(1)
     _check(lib().bastion_budget_select(_ptr(ahat), _ptr(n_avail), B, W1 - 1, nmin, _ptr(cost),
                                        cstride, l_ar, _ptr(nstar), _ptr(s), _stream()),
            "bastion_budget_select")
@@ -219,7 +299,13 @@ def budget_select(ahat, n_avail, nmin: int, cost, l_ar: float = 1.0, with_curve:
 
 
 def tree_mask(parent, n_nodes, pos_base=None):
+    if parent.dim() != 2:
+        raise ValueError("parent must be [B, nmax+1]")
     B, W1 = parent.shape
+    _need(parent, "parent", torch.int32)
+    _need(n_nodes, "n_nodes", torch.int32, (B,), parent.device)
+    if pos_base is not None:
+        _need(pos_base, "pos_base", torch.int32, (B,), parent.device)
     W = (W1 + 31) // 32
     mask = torch.empty((B, W1, W), dtype=torch.int32, device=parent.device)
     pos = torch.empty((B, W1), dtype=torch.int32, device=parent.device)
@@ -229,8 +315,14 @@ def tree_mask(parent, n_nodes, pos_base=None):
 
 
 def accept(parent, token, n_nodes, b: int, target):
+    if parent.dim() != 2:
+        raise ValueError("parent must be [B, nmax+1]")
     B, W1 = parent.shape
     dev = parent.device
+    _need(parent, "parent", torch.int32)
+    _need(token, "token", torch.int32, (B, W1), dev)
+    _need(n_nodes, "n_nodes", torch.int32, (B,), dev)
+    _need(target, "target", torch.int32, (B, W1), dev)
     alen = torch.empty((B,), dtype=torch.int32, device=dev)
     anodes = torch.empty((B, b + 1), dtype=torch.int32, device=dev)
     bonus = torch.empty((B,), dtype=torch.int32, device=dev)
@@ -271,6 +363,16 @@ def _mixture_call(branch_logits, prior_logits, k, nmax, with_tree, with_mask, ou
         tree = alloc_tree_out(B, b, k, nmax, x.device, with_rows=False, with_mask=with_mask)
     if not with_tree:
         tree = None
+    _need(prior_logits, "prior_logits", torch.float32, (B, K), x.device)
+    C_ = K * k
+    mspec = dict(prior_q=(torch.float32, (B, K)), chain_tokens=(torch.int32, (B, K, b)),
+                 qdep_chain=(torch.float64, (B, K)), cand_count=(torch.int32, (B, b)),
+                 cand_tokens=(torch.int32, (B, b, C_)), cand_q=(torch.float32, (B, b, C_, K)),
+                 row_max=(torch.float32, (B, K, b)), row_sum=(torch.float32, (B, K, b)))
+    for name, (dt, shape) in mspec.items():
+        _need(out[name], name, dt, shape, x.device)
+    if tree is not None:
+        _check_tree_out(tree, B, b, k, nmax, x.device, with_rows=False)
     L = lib()
     w = _workspace(ws, x.device)
     buf = w.get(L.bastion_workspace_bytes(B, K, b, V, k, nmax, dt))

@@ -6,8 +6,11 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "device_common.hpp"
 
+#include "api_internal.hpp"
 #include "build_params.hpp"
 #include "mixture.hpp"
 
@@ -39,29 +42,61 @@ constexpr size_t kRowTicketWords = 49152;            // per-row counters
 constexpr size_t kQueryTicketBase = kRowTicketWords;  // per-query counters
 constexpr size_t kTicketBytes = kTicketWords * 4;
 constexpr int kMaxSegments = 64;
-constexpr int64_t kResidentBlocks = 1024;   // stream blocks resident at once
+constexpr int kBlocksPerCu = 4;   // stream blocks of 256 threads resident per CU
+constexpr int kMaxDevices = 64;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int esize(int dtype) { return dtype == BASTION_BF16 ? 2 : 4; }
+
+// Compute units of the current device, read once per device.
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int v = g_cus[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        g_cus[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+// Launch-plan overrides for tuning and tests (bastion_set_tuning), first
+// taken from BASTION_SEGMENTS / BASTION_SPLIT_TREES when the library loads.
+std::atomic<int> g_force_segments{0};     // > 0: segments per row
+std::atomic<int> g_force_split{-1};       // 0 / 1: trees in the stream launch / their own
+
+struct TuningFromEnv {
+    TuningFromEnv() {
+        const char *e = getenv("BASTION_SEGMENTS");
+        if (e && atoi(e) > 0) g_force_segments.store(atoi(e));
+        e = getenv("BASTION_SPLIT_TREES");
+        if (e) g_force_split.store(atoi(e) != 0 ? 1 : 0);
+    }
+} g_tuning_from_env;
 
 struct Layout {
     size_t row_status, partials, row_ms, mtopk_ids, mtopk_q, total;
     int S;
 };
 
-// Segments per row.  Enough blocks to cover the machine: four resident
-// blocks on each of the 256 CUs, or one per CU when the whole input is small
+// Segments per row.  Enough blocks to cover the machine: kBlocksPerCu
+// resident blocks on each CU, or one per CU when the whole input is small
 // (at most 16 MiB), where every block's fixed latency (start, merge,
 // hand-off) outweighs its streaming.  No segment shorter than 16 KiB (four
-// 16-byte loads per thread).  BASTION_SEGMENTS overrides (tuning).
+// 16-byte loads per thread).
 int plan_segments(int64_t rows, int V, int dtype) {
     const int64_t row_bytes = int64_t(V) * esize(dtype);
-    const int64_t target = rows * row_bytes <= (int64_t(16) << 20) ? 256 : 1024;
+    const int64_t cus = device_cus();
+    const int64_t target = rows * row_bytes <= (int64_t(16) << 20) ? cus : kBlocksPerCu * cus;
     int S = int((target + rows - 1) / rows);
-    const char *env = getenv("BASTION_SEGMENTS");
-    if (env && atoi(env) > 0) S = atoi(env);
-    const int64_t by_size = row_bytes / (env && atoi(env) > 0 ? 4096 : 16384);
+    const int forced = g_force_segments.load(std::memory_order_relaxed);
+    if (forced > 0) S = forced;
+    const int64_t by_size = row_bytes / (forced > 0 ? 4096 : 16384);
     if (S > by_size) S = int(by_size);
     if (S > kMaxSegments) S = kMaxSegments;
     if (S < 1) S = 1;
@@ -69,16 +104,18 @@ int plan_segments(int64_t rows, int V, int dtype) {
     return S;
 }
 
-Layout layout(int64_t rows, int k, int S) {
+// with_mixture: also the row statistics and branch top-k that the
+// latent-mixture call keeps between its two launches
+Layout layout(int64_t rows, int k, int S, bool with_mixture = true) {
     Layout L;
     L.S = S;
     L.row_status = kTicketBytes;
     L.partials = align256(L.row_status + size_t(rows) * 4);
-    // row statistics and branch top-k of the latent-mixture call
     L.row_ms = align256(L.partials + (S > 1 ? size_t(rows) * S * size_t(16 + 8 * k) : 0));
-    L.mtopk_ids = align256(L.row_ms + size_t(rows) * 8);
-    L.mtopk_q = align256(L.mtopk_ids + size_t(rows) * k * 4);
-    L.total = align256(L.mtopk_q + size_t(rows) * k * 4);
+    const size_t mix = with_mixture ? 1 : 0;
+    L.mtopk_ids = align256(L.row_ms + mix * size_t(rows) * 8);
+    L.mtopk_q = align256(L.mtopk_ids + mix * size_t(rows) * k * 4);
+    L.total = align256(L.mtopk_q + mix * size_t(rows) * k * 4);
     return L;
 }
 
@@ -133,11 +170,15 @@ int32_t bastion_workspace_init(void *ws, size_t ws_bytes, void *stream) {
                                              static_cast<hipStream_t>(stream)));
 }
 
-int32_t bastion_build_trees(const void *logits, int32_t dtype, int32_t B, int32_t b, int32_t V,
-                            int64_t row_stride, int32_t k, int32_t nmax, int32_t nmin,
-                            const double *cost, int64_t cost_qstride, double l_ar,
-                            const int32_t *pos_base, const bastion_tree_out *out, void *ws,
-                            size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+// bastion_build_trees on a given scratch area (api_internal.hpp).
+int32_t bastion::build_trees_on(const void *logits, int32_t dtype, int32_t B, int32_t b,
+                                int32_t V, int64_t row_stride, int32_t k, int32_t nmax,
+                                int32_t nmin, const double *cost, int64_t cost_qstride,
+                                double l_ar, const int32_t *pos_base,
+                                const bastion_tree_out *out, void *ws, size_t ws_bytes,
+                                void *stream, ScratchSource scratch) {
     if (!logits || (dtype != BASTION_F32 && dtype != BASTION_BF16)) return BASTION_EINVAL;
     if (!sizes_ok(B, b, V, k, nmax) || nmin < 0 || nmin > nmax) return BASTION_EINVAL;
     if (row_stride < V || (reinterpret_cast<uintptr_t>(logits) % esize(dtype)) != 0)
@@ -146,7 +187,12 @@ int32_t bastion_build_trees(const void *logits, int32_t dtype, int32_t B, int32_
     if (cost && (cost_qstride < 0 || !(l_ar > 0.0) || l_ar > 1e300)) return BASTION_EINVAL;
     const int64_t rows = int64_t(B) * b;
     const int S = plan_segments(rows, V, dtype);
-    const Layout L = layout(rows, k, S);
+    // a library-owned scratch holds only what this call uses
+    const Layout L = layout(rows, k, S, scratch == nullptr);
+    if (scratch) {
+        const int32_t st = scratch(L.total, &ws, &ws_bytes);
+        if (st != BASTION_OK) return st;
+    }
     if (!ws || !aligned16(ws) || ws_bytes < L.total) return BASTION_EWORKSPACE;
 
     BuildParams P;
@@ -170,16 +216,41 @@ int32_t bastion_build_trees(const void *logits, int32_t dtype, int32_t B, int32_
     P.rows_per_query = b;
     P.is_bf16 = dtype == BASTION_BF16;
     P.row_ms = nullptr;
+    P.resident_blocks = kBlocksPerCu * device_cus();
     // trees in a launch of their own (one block of 16 waves per query) when
-    // the stream grid fills the machine more than once (256 CUs x 4 blocks),
-    // where a tree would hold a slot that later rows wait for; otherwise the
-    // whole call is one kernel
-    P.split_trees = rows * S > kResidentBlocks ? 1 : 0;
-    {
-        const char *env = getenv("BASTION_SPLIT_TREES");
-        if (env) P.split_trees = atoi(env) != 0;
+    // the stream grid fills the machine more than once, where a tree would
+    // hold a slot that later rows wait for; otherwise the whole call is one
+    // kernel
+    P.split_trees = rows * S > P.resident_blocks ? 1 : 0;
+    const int forced = g_force_split.load(std::memory_order_relaxed);
+    if (forced >= 0) P.split_trees = forced;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (scratch) {
+        // a library-owned scratch keeps the last call's contents: clear the
+        // arrival counters first (with a kernel, so that a caller may
+        // capture the call in a graph)
+        const hipError_t e = bastion_launch_fill_u32(reinterpret_cast<uint32_t *>(w), kTicketWords,
+                                                     0u, s);
+        if (e != hipSuccess) return BASTION_EHIP;
     }
-    return to_status(bastion_launch_build(P, dtype, static_cast<hipStream_t>(stream), nullptr));
+    return to_status(bastion_launch_build(P, dtype, s, nullptr));
+}
+
+extern "C" {
+
+int32_t bastion_build_trees(const void *logits, int32_t dtype, int32_t B, int32_t b, int32_t V,
+                            int64_t row_stride, int32_t k, int32_t nmax, int32_t nmin,
+                            const double *cost, int64_t cost_qstride, double l_ar,
+                            const int32_t *pos_base, const bastion_tree_out *out, void *ws,
+                            size_t ws_bytes, void *stream) {
+    return bastion::build_trees_on(logits, dtype, B, b, V, row_stride, k, nmax, nmin, cost,
+                                   cost_qstride, l_ar, pos_base, out, ws, ws_bytes, stream,
+                                   nullptr);
+}
+
+void bastion_set_tuning(int32_t segments, int32_t split_trees) {
+    g_force_segments.store(segments > 0 ? segments : 0);
+    g_force_split.store(split_trees < 0 ? -1 : (split_trees != 0 ? 1 : 0));
 }
 
 int32_t bastion_budget_select(const double *ahat, const int32_t *n_avail, int32_t B, int32_t nmax,
@@ -260,6 +331,7 @@ int32_t bastion_mixture_score(const void *branch_logits, int32_t dtype, const fl
     P.rows_per_query = K * b;
     P.is_bf16 = dtype == BASTION_BF16;
     P.row_ms = reinterpret_cast<float *>(w + L.row_ms);
+    P.resident_blocks = kBlocksPerCu * device_cus();
     P.prior = prior_logits;
     P.prior_q = mix->prior_q;
     P.chain_tokens = mix->chain_tokens;

@@ -40,6 +40,7 @@ struct BuildParams {
     float *cand_q;
     int mix_tree;         // 1: build the mixture tree into parent/depth/...
     int split_trees;      // 1: the trees run in a launch of their own (mode 0)
+    int resident_blocks;  // stream blocks the machine holds at once
 };
 
 }  // namespace bastion

@@ -321,7 +321,7 @@ __device__ SegmentResult stream_segment(const BuildParams &P, const char *row, i
         // CU), blocks dispatched later (the grid is dispatched in order, over
         // several microseconds) keep a higher priority for longer, by one
         // tier per quarter of the grid.
-        const int age = gridDim.x <= 1024u ? int((blockIdx.x * 4u) / gridDim.x) : 0;
+        const int age = int(gridDim.x) <= P.resident_blocks ? int((blockIdx.x * 4u) / gridDim.x) : 0;
         int tier = -1;
         for (int t = 0; t < ntot; t += 2) {
             int nt = (4 * t) / ntot - age;
@@ -1103,6 +1103,9 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
                 }
                 __syncthreads();
                 const int nsc = s_ns;
+                // every thread has read the count before the next chunk adds
+                // to it, so that all threads take the same branch below
+                __syncthreads();
                 // merge when the buffer could not take another chunk, at the
                 // end of the round, and while the list is not full
                 if (nsc > 0 && (nsc > kMixSurv - CH || base + CH >= total || nR < nmax)) {
@@ -1323,10 +1326,16 @@ hipError_t bastion_launch_build(const bastion::BuildParams &P, int dtype, hipStr
     using namespace bastion;
     constexpr int U = 4;
     const int stream_smem = int(sizeof(WaveScratch<U>)) * kWavesPerBlock;
+    BuildParams Q = P;
+    // trees whose LDS exceeds what a stream block may hold without an
+    // attribute (64 KiB; only b = 32, k = 32 with 257 <= nmax <= 512) run in
+    // the trees' own launch, which requests its LDS explicitly
+    if (Q.mode == 0 && !Q.split_trees && tree_layout(Q.b, Q.k, Q.nmax).total > 65536)
+        Q.split_trees = 1;
     // the mixture stage has a launch of its own
-    const int tree_smem = (P.mode == 1 || P.split_trees) ? 0 : tree_layout(P.b, P.k, P.nmax).total;
+    const int tree_smem = (Q.mode == 1 || Q.split_trees) ? 0 : tree_layout(Q.b, Q.k, Q.nmax).total;
     const int smem = stream_smem > tree_smem ? stream_smem : tree_smem;
     if (smem_out) *smem_out = smem;
-    if (dtype == BASTION_BF16) return launch_r<__bf16, U>(P, smem, s);
-    return launch_r<float, U>(P, smem, s);
+    if (dtype == BASTION_BF16) return launch_r<__bf16, U>(Q, smem, s);
+    return launch_r<float, U>(Q, smem, s);
 }

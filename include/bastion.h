@@ -42,7 +42,23 @@
  *  - rho is a float32 product with one rounding per factor,
  *    rho(child) = fl32(rho(parent) * q); A_hat and S(N) are float64.
  *  - Limits: 1 <= b <= 32, 1 <= k <= 32, k <= V <= 524288, 1 <= nmax <= 1023,
- *    0 <= nmin <= nmax, 1 <= K <= 16.
+ *    0 <= nmin <= nmax, 1 <= K <= 16, B <= 16384.  V is bounded by the
+ *    19-bit token field of the pop-order keys and B by the launch grid.
+ *
+ * Where the calls differ from the plain statement of the problem (logits
+ * in, a budgeted prefix-closed tree out, accepted length after
+ * verification), and why:
+ *  - bastion_build_trees takes pos_base and fills the verifier's mask and
+ *    position ids inside the same launch when out->mask is set: the tree is
+ *    still in LDS there, so the mask costs no second pass over the tree.
+ *  - bastion_budget_select takes n_avail: a recorded A_hat curve may end
+ *    before nmax (a candidate tree smaller than the budget).
+ *  - bastion_tree_mask takes no depth array: depth is recounted along the
+ *    parent links, so a malformed link cannot desynchronise the two.
+ *  - bastion_mixture_score takes row_stride (as bastion_build_trees does)
+ *    and returns its per-branch outputs in a struct, since they are many.
+ *  - bastion_build_trees and bastion_mixture_score take a caller-owned
+ *    workspace (the library allocates nothing).
  */
 #ifndef BASTION_H
 #define BASTION_H
@@ -196,6 +212,16 @@ int32_t bastion_accept(const int32_t *parent, const int32_t *token, const int32_
                        int32_t B, int32_t b, int32_t nmax, const int32_t *target,
                        int32_t *accept_len, int32_t *accept_nodes, int32_t *bonus,
                        void *stream);
+
+/*
+ * bastion_set_tuning -- launch-plan overrides for tuning and tests, not
+ * part of the method: segments > 0 splits every row over that many blocks,
+ * split_trees 0 / 1 forces the trees into the streaming launch / a launch
+ * of their own; 0 and -1 restore the library's own plan.  Process-wide; the
+ * environment variables BASTION_SEGMENTS and BASTION_SPLIT_TREES set the
+ * initial values when the library loads.  Outputs do not depend on it.
+ */
+void bastion_set_tuning(int32_t segments, int32_t split_trees);
 
 /*
  * Outputs of the latent-mixture call.  C = K * k candidate slots per

@@ -18,7 +18,7 @@ def L():
 
 def declared():
     txt = open(HEADER).read()
-    return re.findall(r"^\s*(?:int32_t|size_t|const char \*)\s*\**(bastion_\w+)\s*\(", txt, re.M)
+    return re.findall(r"^\s*(?:int32_t|size_t|void|const char \*)\s*\**(bastion_\w+)\s*\(", txt, re.M)
 
 
 def test_exports_every_declared_symbol(L):
@@ -144,3 +144,25 @@ def test_no_shared_code_between_library_and_reference():
             txt = open(os.path.join(ROOT, "oracle", f)).read()
             assert "block_diffusion_tree_amd" not in txt, f
             assert "bastion.h" not in txt and "libbastion" not in txt, f
+
+
+def test_binding_rejects_bad_cost_tables():
+    """The binding checks a cost table's shape before anything reaches the
+    library: a [B, nmax] table (one column short) would shift every C(n)."""
+    import torch
+    from block_diffusion_tree_amd import binding
+    B, nmax = 4, 16
+    for bad, what in ((torch.zeros(B, nmax, dtype=torch.float64), "columns"),
+                      (torch.zeros(3, nmax + 1, dtype=torch.float64), "rows"),
+                      (torch.zeros(B, 2, nmax + 1, dtype=torch.float64), "cost must be")):
+        with pytest.raises(ValueError, match=what):
+            binding._cost_stride(bad, B, nmax, None)
+    with pytest.raises(TypeError):
+        binding._cost_stride(torch.zeros(B, nmax + 1, dtype=torch.float32), B, nmax, None)
+    with pytest.raises(ValueError, match="GPU"):   # right shape, but on the host
+        binding._cost_stride(torch.zeros(B, nmax + 1, dtype=torch.float64), B, nmax, None)
+
+
+def test_tuning_hook_is_exported(L):
+    L.bastion_set_tuning(3, 1)
+    L.bastion_set_tuning(0, -1)

@@ -1,8 +1,6 @@
 """GPU parity of bastion_build_trees (and the standalone tree kernels) against
 the CPU reference: exact top-k ids, trees, masks, positions and accepts;
 q and row sums within 1e-5 relative; the tree stage fed the GPU's own q."""
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -18,7 +16,7 @@ pytestmark = pytest.mark.gpu
 def _gpu():
     gc.require_gpu()
     yield
-    os.environ.pop("BASTION_SEGMENTS", None)
+    binding.set_tuning(0, -1)
 
 
 def test_tiny_workload_full_parity():
@@ -35,7 +33,7 @@ def test_tiny_workload_full_parity():
 @pytest.mark.parametrize("segments", ["1", "3", "17"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_ragged_multi_segment(segments, dtype):
-    os.environ["BASTION_SEGMENTS"] = segments
+    binding.set_tuning(segments=int(segments))
     wl = synth.scaled(synth.WORKLOADS["main"], B=3, b=5, V=50003, dtype=dtype, nmax=40)
     x = gc.device_logits(wl, seed=7)
     gc.run_and_check(x, wl.k, wl.nmax)
@@ -141,11 +139,11 @@ def test_split_and_fused_trees_agree(shape):
     wl = synth.scaled(synth.WORKLOADS["main"], **shape)
     x = gc.device_logits(wl, seed=9)
     fused = binding.build_trees(x, k=wl.k, nmax=wl.nmax)
-    os.environ["BASTION_SPLIT_TREES"] = "1"
+    binding.set_tuning(split_trees=1)
     try:
         split = binding.build_trees(x, k=wl.k, nmax=wl.nmax)
     finally:
-        os.environ.pop("BASTION_SPLIT_TREES", None)
+        binding.set_tuning(0, -1)
     torch.cuda.synchronize()
     for f in fused:
         assert torch.equal(fused[f], split[f]), f
