@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="main", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the warm-input, accept and streaming-ceiling timings "
+                         "(profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device-to-device copy of this many MiB "
                          "(the reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -71,48 +74,139 @@ def out_bytes(out) -> int:
     return int(sum(t.numel() * t.element_size() for t in out.values()))
 
 
-def cpu_baseline(x_host, wl, n_queries, min_seconds=2.0, max_reps=10):
-    """The CPU reference on the first n_queries queries of the batch, repeated
-    until at least min_seconds of wall time; the median pass is reported."""
+def _oracle_pass(sample, wl, cost=None):
     from oracle import oracle
     import numpy as np
-    sample = x_host[:n_queries]
-    times, rows = [], None
+    rows = oracle.softmax_topk(sample, k=wl.k)
+    tree = oracle.best_first(rows["topk_ids"], rows["topk_p"].astype(np.float32),
+                             nmax=wl.nmax, nmin=wl.nmin,
+                             cost=None if cost is None else cost[:sample.shape[0]],
+                             row_status=rows["row_status"])
+    oracle.tree_mask(tree["parent"], tree["n_nodes"])
+    return rows
+
+
+def _timed(fn, min_seconds, max_reps):
+    import numpy as np
+    times, res = [], None
     while len(times) < max_reps and (sum(times) < min_seconds or len(times) < 2):
         t0 = time.perf_counter()
-        rows = oracle.softmax_topk(sample, k=wl.k)
-        tree = oracle.best_first(rows["topk_ids"], rows["topk_p"].astype(np.float32),
-                                 nmax=wl.nmax, row_status=rows["row_status"])
-        oracle.tree_mask(tree["parent"], tree["n_nodes"])
+        res = fn()
         times.append(time.perf_counter() - t0)
-    dt = float(np.median(times))
-    return dict(value=n_queries / dt, unit="trees/s", cores=oracle.num_threads(), kind="oracle",
+    return float(np.median(times)), len(times), res
+
+
+def cpu_baseline(x_host, wl, n_queries, cost=None, min_seconds=2.0, max_reps=10, n_single=4):
+    """The CPU reference on the first n_queries queries of the batch with all
+    host threads, repeated until at least min_seconds of wall time (the
+    median pass is reported), and on the first n_single queries with one
+    thread."""
+    from oracle import oracle
+    n_single = min(n_single, n_queries)
+    threads = oracle.num_threads()
+    dt, reps, rows = _timed(lambda: _oracle_pass(x_host[:n_queries], wl, cost), min_seconds,
+                            max_reps)
+    oracle.set_num_threads(1)
+    try:
+        dt1, reps1, _ = _timed(lambda: _oracle_pass(x_host[:n_single], wl, cost), 0.5, 3)
+    finally:
+        oracle.set_num_threads(threads)
+    return dict(value=n_queries / dt, unit="trees/s", cores=threads, kind="oracle",
                 sample=f"first {n_queries} of {wl.B} queries of the timed batch "
                        f"({n_queries * wl.b} rows): float64 softmax + top-k, best-first tree, "
-                       f"mask; median of {len(times)} passes, {dt:.3f} s per pass"), rows
+                       f"mask; median of {reps} passes, {dt:.3f} s per pass",
+                single_thread_value=n_single / dt1,
+                single_thread_sample=f"first {n_single} queries, one thread: median of "
+                                     f"{reps1} passes, {dt1:.3f} s per pass"), rows
 
 
-def cpu_baseline_mixture(x, prior, wl, mout, n_queries, min_seconds=2.0, max_reps=10):
-    """The CPU reference of the mixture call on the first n_queries queries."""
+def cpu_baseline_mixture(x, prior, wl, mout, n_queries, min_seconds=2.0, max_reps=10,
+                         n_single=1):
+    """The CPU reference of the mixture call on the first n_queries queries
+    (all host threads) and on the first n_single (one thread)."""
     from oracle import oracle
     import numpy as np
     xs = oracle.host_logits(x[:n_queries])
     ps = prior[:n_queries].cpu().numpy()
-    times, m = [], None
-    while len(times) < max_reps and (sum(times) < min_seconds or len(times) < 2):
-        t0 = time.perf_counter()
-        m = oracle.mixture(xs, ps, k=wl.k)
+
+    def one(n):
+        m = oracle.mixture(xs[:n], ps[:n], k=wl.k)
         oracle.mixture_tree(m["prior_w"].astype(np.float32), m["cand_count"], m["cand_tokens"],
                             m["cand_p"].astype(np.float32), nmax=wl.nmax,
                             row_status=m["row_status"])
-        times.append(time.perf_counter() - t0)
-    dt = float(np.median(times))
+        return m
+    threads = oracle.num_threads()
+    dt, reps, m = _timed(lambda: one(n_queries), min_seconds, max_reps)
+    oracle.set_num_threads(1)
+    try:
+        dt1, reps1, _ = _timed(lambda: one(n_single), 0.5, 2)
+    finally:
+        oracle.set_num_threads(threads)
     ok = bool((mout["chain_tokens"][:n_queries].cpu().numpy() == m["chain_tokens"]).all())
-    return dict(value=n_queries / dt, unit="trees/s", cores=oracle.num_threads(), kind="oracle",
+    return dict(value=n_queries / dt, unit="trees/s", cores=threads, kind="oracle",
                 sample=f"first {n_queries} of {wl.B} queries of the timed batch "
                        f"({n_queries * wl.K * wl.b} branch rows): float64 softmax + top-k, "
                        f"chains and q_dep, candidate unions, mixture tree; median of "
-                       f"{len(times)} passes, {dt:.3f} s per pass"), ok
+                       f"{reps} passes, {dt:.3f} s per pass",
+                single_thread_value=n_single / dt1,
+                single_thread_sample=f"first {n_single} queries, one thread: median of "
+                                     f"{reps1} passes, {dt1:.3f} s per pass"), ok
+
+
+def stream_ceiling(bufs, dev, reps=20):
+    """The practical HBM read rate: a plain streaming-read kernel
+    (libbastion_probe.so) over the same input buffers, rotating like the
+    timed steps, for a few grid sizes; the best rate in GB/s and its grid."""
+    import ctypes as C
+    import numpy as np
+    import torch
+    from block_diffusion_tree_amd import build as hipbuild
+    if not os.path.exists(hipbuild.PROBE_LIB):
+        return None
+    L = C.CDLL(hipbuild.PROBE_LIB)
+    L.bastion_probe_stream_read.restype = C.c_int32
+    L.bastion_probe_stream_read.argtypes = [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p,
+                                            C.c_void_p]
+    nbytes = bufs[0].numel() * bufs[0].element_size()
+    nbytes -= nbytes % 16
+    stream = torch.cuda.current_stream()
+    sp = C.c_void_p(stream.cuda_stream)
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    best = None
+    for blocks in (1024, 2048, 4096, 8192):
+        def go(i):
+            st = L.bastion_probe_stream_read(C.c_void_p(bufs[i % len(bufs)].data_ptr()), nbytes,
+                                             blocks, C.c_void_p(sink.data_ptr()), sp)
+            if st != 0:
+                raise RuntimeError(f"stream probe failed ({st})")
+        for i in range(3):
+            go(i)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for i in range(reps):
+            ev[i][0].record(stream)
+            go(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+        gbs = nbytes / (us * 1e-6) / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = dict(gbs=gbs, us=us, blocks=blocks, bytes=nbytes)
+    return best
+
+
+def time_launches(fn, n, stream):
+    """HIP events around each of n calls of fn(i) on `stream`: times in ms."""
+    import numpy as np
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
 
 
 def main():
@@ -176,6 +270,30 @@ def main():
     wall = time.perf_counter() - t0
     launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
 
+    extras = {}
+    if not args.no_extras:
+        # warm: the same input batch every call (what the MALL keeps of it)
+        warm_ms = time_launches(lambda i: calls[0](), max(10, args.steps // 2), stream)
+        extras["warm"] = {"launch_us_mean": float(warm_ms.mean()) * 1e3,
+                          "launch_us_p50": float(np.median(warm_ms)) * 1e3,
+                          "launch_us_p10": float(np.percentile(warm_ms, 10)) * 1e3,
+                          "launch_us_p90": float(np.percentile(warm_ms, 90)) * 1e3}
+        if not mixture:
+            # bastion_accept on the trees of buffer 0, timed on its own
+            o = outs[0]
+            top1 = o["topk_ids"][:, :, 0].cpu().numpy()
+            tgt = synth.make_targets(o["parent"].cpu().numpy(), o["token"].cpu().numpy(),
+                                     o["depth"].cpu().numpy(), o["n_nodes"].cpu().numpy(),
+                                     top1, wl.V, seed=wl.seed)
+            tgt = torch.from_numpy(tgt).to(dev)
+            acc_ms = time_launches(lambda i: binding.accept(o["parent"], o["token"], o["n_nodes"],
+                                                            wl.b, tgt), 30, stream)
+            alen = binding.accept(o["parent"], o["token"], o["n_nodes"], wl.b, tgt)[0]
+            extras["accept"] = {"launch_us_mean": float(acc_ms.mean()) * 1e3,
+                                "launch_us_p50": float(np.median(acc_ms)) * 1e3,
+                                "mean_accept_len": float(alen.float().mean())}
+        extras["ceiling"] = stream_ceiling(bufs, dev)
+
     ms_per_step = wall * 1e3 / args.steps
     alg_bytes = wl.logit_bytes + out_bytes(outs[0])
     if mixture:
@@ -214,6 +332,19 @@ def main():
                      "launch_us_p10": float(np.percentile(launch_ms, 10)) * 1e3,
                      "launch_us_p90": float(np.percentile(launch_ms, 90)) * 1e3},
     }
+    ceil = extras.get("ceiling")
+    if ceil:
+        line["roofline"]["ceiling"] = {
+            "achieved_read_gbs": ceil["gbs"], "grid_blocks": ceil["blocks"],
+            "kernel": "stream_read_chunks (libbastion_probe.so): the same input buffers read "
+                      "once with the same 16-byte loads and nothing else",
+            "frac_of_ceiling": achieved / ceil["gbs"]}
+    if "warm" in extras:
+        w = extras["warm"]
+        w["achieved_gbs"] = alg_bytes / (w["launch_us_mean"] * 1e-6) / 1e9
+        line["warm"] = w
+    if "accept" in extras:
+        line["accept"] = extras["accept"]
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -232,7 +363,8 @@ def main():
         else:
             x_host = oracle.host_logits(bufs[0])
             n_q = wl.B
-            base, rows = cpu_baseline(x_host, wl, n_q)
+            base, rows = cpu_baseline(x_host, wl, n_q,
+                                      cost=None if cost is None else cost.cpu().numpy())
             line["cpu_baseline"] = base
             # the timed GPU outputs of buffer 0 agree with the reference sample
             g_ids = outs[0]["topk_ids"][:n_q].cpu().numpy()

@@ -369,8 +369,8 @@ def _mixture_call(branch_logits, prior_logits, k, nmax, with_tree, with_mask, ou
                  qdep_chain=(torch.float64, (B, K)), cand_count=(torch.int32, (B, b)),
                  cand_tokens=(torch.int32, (B, b, C_)), cand_q=(torch.float32, (B, b, C_, K)),
                  row_max=(torch.float32, (B, K, b)), row_sum=(torch.float32, (B, K, b)))
-    for name, (dt, shape) in mspec.items():
-        _need(out[name], name, dt, shape, x.device)
+    for name, (tdt, shape) in mspec.items():
+        _need(out[name], name, tdt, shape, x.device)
     if tree is not None:
         _check_tree_out(tree, B, b, k, nmax, x.device, with_rows=False)
     L = lib()

@@ -64,8 +64,10 @@ int oracle_abi_version(void) { return 1; }
 #ifdef _OPENMP
 #include <omp.h>
 int oracle_num_threads(void) { return omp_get_max_threads(); }
+void oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int oracle_num_threads(void) { return 1; }
+void oracle_set_num_threads(int n) { (void)n; }
 #endif
 
 /* bf16 is the upper half of an IEEE binary32. */

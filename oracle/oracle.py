@@ -53,6 +53,8 @@ I32, I64, F64 = C.c_int, C.c_int64, C.c_double
 def _declare(L):
     L.oracle_abi_version.restype = I32
     L.oracle_num_threads.restype = I32
+    L.oracle_set_num_threads.argtypes = [I32]
+    L.oracle_set_num_threads.restype = None
     L.oracle_softmax_topk.argtypes = [P, I32, I64, I32, I64, I32, P, P, P, P, P]
     L.oracle_best_first.argtypes = [P, P, P, I32, I32, I32, I32, I32, P, I64, F64,
                                     P, P, P, P, P, P, P]
@@ -72,6 +74,11 @@ def _declare(L):
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of the following calls (timing the reference only)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def _p(a):

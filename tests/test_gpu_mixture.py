@@ -79,13 +79,15 @@ def test_mixture_workload_slice_full_parity():
     assert (gc.np_(tr["qstatus"]) == 0).all()
 
 
-def test_mixture_full_workload_sampled_parity():
-    """The whole latent-mixture workload in one call (the benchmark's launch);
-    the reference checks three of its queries."""
+def test_mixture_full_workload_full_parity():
+    """The whole latent-mixture workload in one call (the benchmark's launch),
+    every query checked: rows, chains, q_dep, candidate unions and q, and
+    every mixture tree, mask and position."""
     wl = synth.WORKLOADS["mixture"]
     x = synth.make_logits(wl, device="cuda")
     prior = synth.make_prior_logits(wl, device="cuda")
-    check_mixture(x, prior, wl.k, wl.nmax, queries=[0, 61, wl.B - 1])
+    mo, tr, _ = check_mixture(x, prior, wl.k, wl.nmax)
+    assert (gc.np_(tr["qstatus"]) == 0).all()
     del x
     torch.cuda.empty_cache()
 
