@@ -283,6 +283,35 @@ def prepare_build_trees(logits, k: int, nmax: int, nmin: int = 1, cost=None, l_a
     return _build_trees_call(logits, k, nmax, nmin, cost, l_ar, pos_base, with_mask, out, ws)
 
 
+def build_trees_noalloc(logits, k: int, nmax: int, nmin: int = 1, cost=None, l_ar: float = 1.0,
+                        pos_base=None, with_mask: bool = True, out=None):
+    """bastion_build_trees_noalloc: the same call on the library's own per-GPU
+    scratch (no workspace; the C call allocates nothing).  Calls that overlap
+    on one GPU race on that scratch."""
+    _dev(logits, "logits")
+    if logits.dim() != 3 or logits.stride(2) != 1 or logits.stride(0) != logits.size(1) * logits.stride(1):
+        raise ValueError("logits must be [B, b, V] with unit stride over V and rows packed")
+    B, b, V = logits.shape
+    dt = _dtype_code(logits)
+    if out is None:
+        out = alloc_tree_out(B, b, k, nmax, logits.device, with_mask=with_mask)
+    cost_ptr, cstride = None, 0
+    if cost is not None:
+        cstride = _cost_stride(cost, B, nmax, logits.device)
+        cost_ptr = _ptr(cost)
+    if pos_base is not None:
+        _need(pos_base, "pos_base", torch.int32, (B,), logits.device)
+    _check_tree_out(out, B, b, k, nmax, logits.device, with_rows=True)
+    fn = lib().bastion_build_trees_noalloc
+    fn.restype = I32
+    fn.argtypes = [P, I32, I32, I32, I32, I64, I32, I32, I32, P, I64, F64, P,
+                   C.POINTER(TreeOut), P]
+    st = _tree_struct(out)
+    _check(fn(_ptr(logits), dt, B, b, V, logits.stride(1), k, nmax, nmin, cost_ptr, cstride, l_ar,
+              _ptr(pos_base), C.byref(st), _stream()), "bastion_build_trees_noalloc")
+    return out
+
+
 def budget_select(ahat, n_avail, nmin: int, cost, l_ar: float = 1.0, with_curve: bool = True):
     if ahat.dim() != 2:
         raise ValueError("ahat must be [B, nmax+1]")

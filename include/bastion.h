@@ -169,6 +169,29 @@ int32_t bastion_build_trees(const void *logits, int32_t dtype, int32_t B, int32_
                             void *stream);
 
 /*
+ * bastion_build_trees_noalloc -- bastion_build_trees for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments and outputs
+ * without the workspace: the call's scratch is a 4 MiB device array inside
+ * the library, one copy per GPU, held until the process ends.  The call
+ * allocates nothing; it clears the array's arrival counters with a kernel
+ * on `stream` before its own launch.  Every call on a GPU shares that GPU's
+ * array, so calls that overlap in time on one GPU (other streams, other
+ * host threads) race and must be serialised by the caller.
+ * Errors: as bastion_build_trees, plus EUNSUPPORTED when the call's launch
+ * plan needs more than bastion_noalloc_scratch_bytes() of scratch (it needs
+ * 256 KiB + 4 bytes per row, plus per-segment records when rows are split,
+ * about 0.5 MiB at B = 256, b = 16); EHIP if the array's device address
+ * cannot be obtained.
+ */
+int32_t bastion_build_trees_noalloc(const void *logits, int32_t dtype, int32_t B, int32_t b,
+                                    int32_t V, int64_t row_stride, int32_t k, int32_t nmax,
+                                    int32_t nmin, const double *cost, int64_t cost_qstride,
+                                    double l_ar, const int32_t *pos_base,
+                                    const bastion_tree_out *out, void *stream);
+size_t bastion_noalloc_scratch_bytes(void);
+
+/*
  * bastion_budget_select -- [BASTION] Methodology 3 on a recorded A_hat curve.
  * ahat [B, nmax+1] (entries 0..n_avail[q] valid, e.g. from a fixed-budget
  * build); cost as in bastion_build_trees.  nstar[q] = the first
