@@ -44,6 +44,15 @@ class MixOut(C.Structure):
                                  "cand_tokens", "cand_q", "row_max", "row_sum")]
 
 
+def use_library(path: str):
+    """Load `path` instead of libbastion.so (the stamped build of the same
+    sources); must come before the first call."""
+    global LIB_PATH
+    if _lib is not None:
+        raise RuntimeError("the library is already loaded")
+    LIB_PATH = path
+
+
 def lib():
     """The loaded library (torch's HIP runtime is loaded first, so both share it)."""
     global _lib

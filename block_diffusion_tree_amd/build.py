@@ -37,9 +37,10 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, outdir: str = None, extra=()) -> str:
+    outdir = outdir or BUILD
+    obj = os.path.join(outdir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC] + FLAGS + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(line for line in r.stderr.splitlines()
                      if "packed-fp32-ops" not in line)
@@ -71,5 +72,26 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# The stamped library: the same sources compiled with -DBASTION_STAMPS, which
+# adds per-block timestamps and bastion_debug_set_stamps (phase tables of
+# `python -m block_diffusion_tree_amd.stamps`).  Not the product library.
+STAMPS_LIB = os.path.join(PKG, "libbastion_stamps.so")
+
+
+def build_stamped(verbose: bool = False) -> str:
+    out = os.path.join(BUILD, "stamps")
+    os.makedirs(out, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(lambda f: _compile(f, out, ["-DBASTION_STAMPS"]), SOURCES))
+    _link(objs, STAMPS_LIB)
+    if verbose:
+        print("built", STAMPS_LIB)
+    return STAMPS_LIB
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    import sys as _sys
+    if "--stamps" in _sys.argv:
+        build_stamped(verbose=True)
+    else:
+        build(verbose=True)

@@ -79,6 +79,22 @@ struct TuningFromEnv {
     }
 } g_tuning_from_env;
 
+#ifdef BASTION_STAMPS
+// stamped build: the timestamp buffer of the following calls (device)
+uint64_t *g_stamps = nullptr;
+#endif
+
+// timestamps of a call whose stream launch has `grid` blocks
+void set_stamps(BuildParams &P, int64_t grid) {
+#ifdef BASTION_STAMPS
+    P.stamps = g_stamps;
+    P.stamp_second = grid;
+#else
+    (void)P;
+    (void)grid;
+#endif
+}
+
 struct Layout {
     size_t row_status, partials, row_ms, mtopk_ids, mtopk_q, total;
     int S;
@@ -217,6 +233,7 @@ int32_t bastion::build_trees_on(const void *logits, int32_t dtype, int32_t B, in
     P.is_bf16 = dtype == BASTION_BF16;
     P.row_ms = nullptr;
     P.resident_blocks = kBlocksPerCu * device_cus();
+    set_stamps(P, rows * S);
     // trees in a launch of their own (one block of 16 waves per query) when
     // the stream grid fills the machine more than once, where a tree would
     // hold a slot that later rows wait for; otherwise the whole call is one
@@ -247,6 +264,13 @@ int32_t bastion_build_trees(const void *logits, int32_t dtype, int32_t B, int32_
                                    cost_qstride, l_ar, pos_base, out, ws, ws_bytes, stream,
                                    nullptr);
 }
+
+#ifdef BASTION_STAMPS
+// Stamped build only: per-block timestamps of the following calls go to
+// `buf` (device, kStampSlots words per block of the stream launch, then per
+// block of the second launch), or nowhere when buf is NULL.
+void bastion_debug_set_stamps(uint64_t *buf) { g_stamps = buf; }
+#endif
 
 void bastion_set_tuning(int32_t segments, int32_t split_trees) {
     g_force_segments.store(segments > 0 ? segments : 0);
@@ -332,6 +356,7 @@ int32_t bastion_mixture_score(const void *branch_logits, int32_t dtype, const fl
     P.is_bf16 = dtype == BASTION_BF16;
     P.row_ms = reinterpret_cast<float *>(w + L.row_ms);
     P.resident_blocks = kBlocksPerCu * device_cus();
+    set_stamps(P, rows * S);
     P.prior = prior_logits;
     P.prior_q = mix->prior_q;
     P.chain_tokens = mix->chain_tokens;

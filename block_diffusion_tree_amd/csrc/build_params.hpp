@@ -41,6 +41,9 @@ struct BuildParams {
     int mix_tree;         // 1: build the mixture tree into parent/depth/...
     int split_trees;      // 1: the trees run in a launch of their own (mode 0)
     int resident_blocks;  // stream blocks the machine holds at once
+    uint64_t *stamps;     // stamped build only: per-block timestamps of the
+                          // stream launch, then of the second launch's blocks
+    int64_t stamp_second; // slot-block index where the second launch's start
 };
 
 }  // namespace bastion

@@ -655,8 +655,10 @@ __device__ void emit_tree(const BuildParams &P, int q, const int32_t *par, const
     }
 }
 
+// st: this block's timestamps (stamped build), or null
 template <int G, int NT = kThreads>
-__device__ void tree_stage(const BuildParams &P, int q, char *smem) {
+__device__ void tree_stage(const BuildParams &P, int q, char *smem, uint64_t *st) {
+    (void)st;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const TreeLayout TL = tree_layout(P.b, P.k, P.nmax, NT);
     RoundsLds S;
@@ -723,6 +725,7 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
     __syncthreads();
     if (rst != BASTION_Q_OK) atomicOr(&s_bad, rst == BASTION_Q_RANGE ? 2 : 1);
     __syncthreads();
+    BASTION_STAMP(st, 4);
     const bool bad = s_bad != 0;
     // a bad row outranks a row outside the float32 range
     const int bad_status = (s_bad & 1) ? BASTION_Q_BAD_LOGITS : BASTION_Q_RANGE;
@@ -744,10 +747,12 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
         F.t0 = ft0;
         FamRegs FR;
         const float bound = family_bound<NT>(S.qtab, S.ttab, F, b, k, kp, nmax, PL.hist, lvl, FR);
+        BASTION_STAMP(st, 5);
         // the family usually holds every node at or above the bound; if not,
         // one wave enumerates them level by level
         const int nf = family_select<NT>(PL, S.qtab, S.ttab, F, FW, FR, b, k, kp, bound,
                                                kPoolCap, lvl);
+        BASTION_STAMP(st, 6);
         if (nf >= 1 && nf <= kPoolCap) {
             FamGeom FG;
             int tot;
@@ -776,6 +781,7 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
         __syncthreads();
     }
 
+    BASTION_STAMP(st, 7);
     if (!bad && wv == 0) {
         if (cnt < 0) cnt = exact_build<G>(S, b, k, nmax);
         if (lane == 0) {
@@ -811,9 +817,11 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem) {
         }
     }
     __syncthreads();
+    BASTION_STAMP(st, 8);
     const int nstar = bad ? 0 : s_nstar;
     const int status = bad ? bad_status : s_status;
     emit_tree<NT>(P, q, S.par, S.dep, S.tok, S.rho, S.ahat, nstar, bad, status);
+    BASTION_STAMP(st, 9);
 }
 
 // Latent-mixture stage of one query (mixture.hpp): prior weights, chains and
@@ -1145,8 +1153,11 @@ __global__ __launch_bounds__(kThreads, (R >= 16 ? 2 : 4)) void build_trees_kerne
     const int q = row / P.rows_per_query;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const char *rowp = P.logits + int64_t(row) * P.row_stride_bytes;
+    BASTION_STAMP(P.stamps, 0);
+    BASTION_STAMP_WHERE(P.stamps);
 
     SegmentResult sr = stream_segment<T, U>(P, rowp, seg, smem);
+    BASTION_STAMP(P.stamps, 1);
     WaveScratch<U> *scr = reinterpret_cast<WaveScratch<U> *>(smem);
     uint64_t *cand = scr[0].cand;
 
@@ -1235,6 +1246,7 @@ __global__ __launch_bounds__(kThreads, (R >= 16 ? 2 : 4)) void build_trees_kerne
             }
         }
     }
+    BASTION_STAMP(P.stamps, 2);
     // latent mixture: the query stage runs in its own launch (mixture_kernel)
     if constexpr (MODE == 1) return;
     // more blocks than fit the machine at once: trees in their own launch
@@ -1244,7 +1256,8 @@ __global__ __launch_bounds__(kThreads, (R >= 16 ? 2 : 4)) void build_trees_kerne
     // wait for its results no more than it waits for them: issue ahead of
     // them (a finished stream leaves this block's waves at priority 0).
     __builtin_amdgcn_s_setprio(3);
-    tree_stage<R>(P, q, smem);
+    BASTION_STAMP(P.stamps, 3);
+    tree_stage<R>(P, q, smem, P.stamps);
 }
 
 // The latent-mixture stage, one block per query, launched after the stream
@@ -1255,7 +1268,10 @@ constexpr int kMixThreads = 1024;   // the stage has a CU to itself: 16 waves pe
 
 __global__ __launch_bounds__(kMixThreads) void mixture_kernel(BuildParams P) {
     extern __shared__ __align__(16) char smem[];
+    uint64_t *st = P.stamps ? P.stamps + P.stamp_second * kStampSlots : nullptr;
+    BASTION_STAMP(st, 3);
     mixture_stage<kMixThreads>(P, int(blockIdx.x), smem);
+    BASTION_STAMP(st, 9);
 }
 
 // The trees of a call whose stream grid does not fit the machine at once,
@@ -1271,7 +1287,9 @@ constexpr int tree_threads() { return R >= 16 ? 512 : 1024; }
 template <int R>
 __global__ __launch_bounds__(tree_threads<R>()) void tree_kernel(BuildParams P) {
     extern __shared__ __align__(16) char smem[];
-    tree_stage<R, tree_threads<R>()>(P, int(blockIdx.x), smem);
+    uint64_t *st = P.stamps ? P.stamps + P.stamp_second * kStampSlots : nullptr;
+    BASTION_STAMP(st, 3);
+    tree_stage<R, tree_threads<R>()>(P, int(blockIdx.x), smem, st);
 }
 
 // ---------------------------------------------------------------------------

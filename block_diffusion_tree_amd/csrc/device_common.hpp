@@ -23,6 +23,31 @@ constexpr int kMaxNmax = 1023; // non-root nodes
 constexpr int kMaxV = 524288;  // tokens (19-bit field in the tree key)
 constexpr int kMaxBranches = 16;
 
+// Block timestamps behind the phase table of the stamped build (compiled
+// with -DBASTION_STAMPS; absent from the product library).  Thread 0 of the
+// block records the 100 MHz real-time counter into its block's slots.
+constexpr int kStampSlots = 16;
+#ifdef BASTION_STAMPS
+#define BASTION_STAMP(stamps, slot)                                                        \
+    do {                                                                                   \
+        if ((stamps) && threadIdx.x == 0)                                                  \
+            (stamps)[size_t(blockIdx.x) * kStampSlots + (slot)] =                          \
+                __builtin_amdgcn_s_memrealtime();                                          \
+    } while (0)
+#define BASTION_STAMP_WHERE(stamps)                                                        \
+    do {                                                                                   \
+        if ((stamps) && threadIdx.x == 0) {                                                \
+            (stamps)[size_t(blockIdx.x) * kStampSlots + 14] =                              \
+                uint64_t(__builtin_amdgcn_s_getreg((3 << 11) | 20));  /* XCC_ID */        \
+            (stamps)[size_t(blockIdx.x) * kStampSlots + 15] =                              \
+                uint64_t(__builtin_amdgcn_s_getreg((31 << 11) | 4));  /* HW_ID */         \
+        }                                                                                  \
+    } while (0)
+#else
+#define BASTION_STAMP(stamps, slot) do { } while (0)
+#define BASTION_STAMP_WHERE(stamps) do { } while (0)
+#endif
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
