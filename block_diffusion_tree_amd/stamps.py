@@ -78,11 +78,16 @@ def analyse(wl, st):
     out["blocks"] = nstream
     out["start"] = us(s[:, 0])
     out["stream_end"] = us(s[:, 1])
-    out["row_done"] = us(s[:, 2])
-    xcc = s[:, 14] & 0xF
+    # a row split over several blocks is finished by the last of them only
+    done = s[:, 2] != 0
+    out["row_done"] = us(s[done, 2])
+    xcc = (s[:, 14] & 0xF)[done]
     out["xcc_p50"] = {int(x): float(np.median(out["row_done"][xcc == x])) for x in np.unique(xcc)}
-    q4 = (np.arange(nstream) * 4) // nstream
-    out["quarter_p50"] = [float(np.median(out["row_done"][q4 == i])) for i in range(4)]
+    q4 = ((np.arange(nstream) * 4) // nstream)[done]
+    out["quarter_p50"] = [float(np.median(out["row_done"][q4 == i])) if (q4 == i).any()
+                          else float("nan") for i in range(4)]
+    out["last_row_done"] = float(out["row_done"].max())
+    out["merge_gap"] = float(out["row_done"].max() - out["stream_end"].max())
     # tree stages: in the stream blocks (slot 3 set there) or in the second launch
     second = st[nstream:]
     second = second[second[:, 3] != 0]
@@ -94,7 +99,9 @@ def analyse(wl, st):
                         if last[a] and last[b]}
     out["last_tree_start"] = float(us(np.array([last[3]]))[0])
     out["tree_total_p50"] = float(np.median((trees[:, end_slot] - trees[:, 3]) / 100.0))
-    out["last_row_done"] = float(out["row_done"].max())
+    # per-phase medians over every tree
+    out["phase_p50"] = {name: float(np.median((trees[:, b] - trees[:, a]) / 100.0))
+                        for a, b, name in TREE_PHASES if (trees[:, a] != 0).all() and (trees[:, b] != 0).all()}
     return out
 
 
@@ -122,11 +129,16 @@ def main():
           " / ".join(f"{med(lambda r, x=x: r['xcc_p50'].get(x, np.nan)):.1f}" for x in xs) + " |")
     print("| row finished p50 by dispatch quarter | " +
           " / ".join(f"{med(lambda r, i=i: r['quarter_p50'][i]):.1f}" for i in range(4)) + " |")
+    print(f"| last row finished after the last stream end | {med(lambda r: r['merge_gap']):.1f} |")
     print(f"| tree stage of the last query: start | {med(lambda r: r['last_tree_start']):.1f} |")
     for _, _, name in TREE_PHASES:
         v = med(lambda r, n=name: r["last_tree"].get(n, np.nan))
         print(f"| ... {name} | {v:.2f} |")
     print(f"| tree stage duration, p50 over queries | {med(lambda r: r['tree_total_p50']):.1f} |")
+    for _, _, name in TREE_PHASES:
+        v = med(lambda r, n=name: r["phase_p50"].get(n, np.nan))
+        print(f"| ... p50 over queries: {name} | {v:.2f} |")
+
     print(f"| last tree done (kernel end) | {med(lambda r: r['kernel_end']):.1f} |")
     sys.stdout.flush()
 
