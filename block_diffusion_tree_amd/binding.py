@@ -370,6 +370,82 @@ def accept(parent, token, n_nodes, b: int, target):
     return alen, anodes, bonus
 
 
+_verify_lib = None
+
+
+def _vlib():
+    """The tree-attention entry points (bastion_verify.h) of the same library."""
+    global _verify_lib
+    if _verify_lib is None:
+        L = lib()
+        L.bastion_tree_attention_workspace_bytes.restype = SZ
+        L.bastion_tree_attention_workspace_bytes.argtypes = [I32] * 5
+        L.bastion_tree_attention.restype = I32
+        L.bastion_tree_attention.argtypes = [P, I64, I32, I32, I32, I32, I32, P, P, I32, P, P, P,
+                                             I32, P, P, P, SZ, P]
+        _verify_lib = L
+    return _verify_lib
+
+
+_attn_ws = {}
+
+
+def rope_inv_freq(theta: float = 1.0e6, head_dim: int = 128, device="cuda"):
+    """Rotary frequencies theta^(-2d/D), d < D/2, computed in float64 and
+    stored as float32 (the table bastion_tree_attention takes)."""
+    import numpy as np
+    d = np.arange(head_dim // 2, dtype=np.float64)
+    return torch.from_numpy((theta ** (-2.0 * d / head_dim)).astype(np.float32)).to(device)
+
+
+def tree_attention(qkv, S: int, T: int, Hq: int, Hkv: int, k_cache, v_cache, ctx_len,
+                   position_ids, mask, inv_freq, out=None, ws=None):
+    """bastion_tree_attention: qkv [S*T, >= (Hq+2Hkv)*128] bf16 rows (unit
+    stride over columns), k_cache [S, Hkv, Lmax, 128] and v_cache
+    [S, Hkv, 128, Lmax] bf16 (the tree tokens are written into them),
+    ctx_len [S] int32, position_ids [S, T] int32, mask [S, T, W] 32-bit words,
+    inv_freq [64] float32.  Returns out [S*T, Hq*128] bf16."""
+    D = 128
+    dev = qkv.device
+    if qkv.dim() != 2 or qkv.stride(1) != 1 or qkv.size(0) != S * T:
+        raise ValueError("qkv must be [S*T, C] with unit column stride")
+    if qkv.dtype != torch.bfloat16 or not qkv.is_cuda:
+        raise TypeError("qkv must be a bfloat16 GPU tensor")
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [S, Hkv, Lmax, 128]")
+    Lmax = k_cache.size(2)
+    W = (T + 31) // 32
+    _need(k_cache, "k_cache", torch.bfloat16, (S, Hkv, Lmax, D), dev)
+    _need(v_cache, "v_cache", torch.bfloat16, (S, Hkv, D, Lmax), dev)
+    _need(ctx_len, "ctx_len", torch.int32, (S,), dev)
+    _need(position_ids, "position_ids", torch.int32, (S, T), dev)
+    if mask.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("mask must hold 32-bit words")
+    _need(mask, "mask", mask.dtype, (S, T, W), dev)
+    _need(inv_freq, "inv_freq", torch.float32, (D // 2,), dev)
+    if out is None:
+        out = torch.empty((S * T, Hq * D), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (S * T, Hq * D), dev)
+    L = _vlib()
+    need = L.bastion_tree_attention_workspace_bytes(S, T, Hq, Hkv, Lmax)
+    if need == 0:
+        raise ValueError("invalid tree-attention sizes")
+    if ws is None:
+        key = (str(dev), torch.cuda.current_stream(dev).cuda_stream)
+        buf = _attn_ws.get(key)
+        if buf is None or buf.numel() < need:
+            buf = torch.empty(need, dtype=torch.uint8, device=dev)
+            _attn_ws[key] = buf
+        ws = buf
+    if ws.numel() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    _check(L.bastion_tree_attention(_ptr(qkv), qkv.stride(0), S, T, Hq, Hkv, D, _ptr(k_cache),
+                                    _ptr(v_cache), Lmax, _ptr(ctx_len), _ptr(position_ids),
+                                    _ptr(mask), W, _ptr(inv_freq), _ptr(out), _ptr(ws), ws.numel(),
+                                    _stream()), "bastion_tree_attention")
+    return out
+
+
 def alloc_mixture_out(B, K, b, k, device):
     C_ = K * k
     i32 = dict(dtype=torch.int32, device=device)

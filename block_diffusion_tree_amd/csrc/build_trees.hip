@@ -1269,6 +1269,7 @@ constexpr int kMixThreads = 1024;   // the stage has a CU to itself: 16 waves pe
 __global__ __launch_bounds__(kMixThreads) void mixture_kernel(BuildParams P) {
     extern __shared__ __align__(16) char smem[];
     uint64_t *st = P.stamps ? P.stamps + P.stamp_second * kStampSlots : nullptr;
+    (void)st;
     BASTION_STAMP(st, 3);
     mixture_stage<kMixThreads>(P, int(blockIdx.x), smem);
     BASTION_STAMP(st, 9);

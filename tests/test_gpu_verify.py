@@ -1,0 +1,106 @@
+"""GPU parity of bastion_tree_attention (the tree's consumer) against the
+float64 reference of oracle/verify_oracle.py.
+
+Tolerance, from the kernel's arithmetic: scores and softmax are float32 and
+the probabilities enter the value product rounded to bf16 (relative error at
+most 2^-9 each), so an output element can move by up to 2^-9 of the largest
+|v| it averages; the output itself is rounded to bf16 (2^-9 relative); the
+rotated q and k are rounded to bf16 from float32 here and from float64 in
+the reference, which rarely picks the neighbouring bf16 value.  Bound used:
+|gpu - ref| <= 2^-8 max|v| + 2^-8 |ref|.  Cached v slots are copied
+exactly; rotated k slots may differ by one bf16 step in rare elements."""
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_tree_amd import binding, synth
+from oracle import verify_oracle as vo
+import gpu_common as gc
+from test_oracle_verify import make_case
+
+pytestmark = pytest.mark.gpu
+
+
+def to_dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dtype).to("cuda")
+
+
+def run_case(S, T, Hq, Hkv, Lmax, ctx, parents, seed, poison=True, mask_pos=None):
+    gc.require_gpu()
+    rng = np.random.default_rng(seed)
+    qkv, kc, vc, ctxa, pos, mask, inv = make_case(rng, S, T, Hq, Hkv, Lmax, ctx, parents)
+    if mask_pos is not None:
+        mask, pos = mask_pos
+    ref, kc_ref, vc_ref = vo.tree_attention(qkv, S, T, Hq, Hkv, 128, kc, vc, ctxa, pos, mask, inv)
+    kcd = to_dev(kc, torch.bfloat16)
+    vcd = to_dev(vc, torch.bfloat16)
+    if poison:
+        # slots past each sequence's keys hold NaN: nothing may read them
+        for s in range(S):
+            end = min(max(int(ctx[s]), 0), Lmax - T) + T
+            kcd[s, :, end:, :] = float("nan")
+            vcd[s, :, :, end:] = float("nan")
+    out = binding.tree_attention(to_dev(qkv, torch.bfloat16), S, T, Hq, Hkv, kcd, vcd,
+                                 to_dev(ctxa, torch.int32), to_dev(pos, torch.int32),
+                                 to_dev(mask.view(np.int32), torch.int32),
+                                 to_dev(inv, torch.float32))
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    vmax = np.abs(qkv[:, (Hq + Hkv) * 128:(Hq + 2 * Hkv) * 128]).max()
+    vmax = max(vmax, np.abs(vc[..., :max(ctx) if max(ctx) > 0 else 1]).max())
+    err = np.abs(got - ref)
+    bound = 2.0 ** -8 * vmax + 2.0 ** -8 * np.abs(ref)
+    assert np.isfinite(got).all()
+    assert (err <= bound).all(), f"max err {err.max()} (bound at worst {bound[err > bound].min()})"
+    # caches: v copied exactly, rotated k within one bf16 step
+    kg = kcd.double().cpu().numpy()
+    vg = vcd.double().cpu().numpy()
+    for s in range(S):
+        c = min(max(int(ctx[s]), 0), Lmax - T)
+        assert np.array_equal(vg[s, :, :, :c + T], vc_ref[s, :, :, :c + T])
+        dk = np.abs(kg[s, :, c:c + T, :] - kc_ref[s, :, c:c + T, :])
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(kc_ref[s, :, c:c + T, :]), 1e-30))) - 7)
+        assert (dk <= ulp).all()
+        assert (dk > 0).mean() < 1e-3
+    return got, ref
+
+
+def random_parents(rng, S, T):
+    return [[-1] + [int(rng.integers(0, i)) for i in range(1, T)] for _ in range(S)]
+
+
+@pytest.mark.parametrize("S,T,Hq,Hkv,Lmax,ctx", [
+    (2, 9, 8, 2, 64, [5, 0]),            # one key split: output written directly
+    (1, 65, 32, 8, 1024, [700]),         # Qwen3-8B heads, N = 64, four splits combined
+    (3, 33, 16, 16, 512, [0, 300, 40]),  # no grouping
+    (1, 129, 16, 1, 256, [100]),         # one KV head for 16 query heads
+    (2, 17, 4, 2, 96, [90, 200]),        # contexts past the cache are clamped
+])
+def test_tree_attention_matches_reference(S, T, Hq, Hkv, Lmax, ctx):
+    rng = np.random.default_rng(T)
+    run_case(S, T, Hq, Hkv, Lmax, ctx, random_parents(rng, S, T), seed=T + S)
+
+
+def test_tree_attention_large_tree():
+    """N = 256 (1028 query rows per KV head, 17 row tiles) behind 2000 tokens."""
+    rng = np.random.default_rng(5)
+    run_case(1, 257, 32, 8, 2304, [2000], random_parents(rng, 1, 257), seed=5)
+
+
+def test_tree_attention_consumes_build_trees_outputs():
+    """The mask and position ids come straight from bastion_build_trees
+    (pos_base = the context length): the layer's input is the library's
+    own verifier input."""
+    gc.require_gpu()
+    wl = synth.scaled(synth.WORKLOADS["main"], B=2, V=20000, nmax=40)
+    x = gc.device_logits(wl)
+    ctx = torch.tensor([333, 17], dtype=torch.int32, device="cuda")
+    g = binding.build_trees(x, k=wl.k, nmax=wl.nmax, pos_base=ctx)
+    torch.cuda.synchronize()
+    parent = gc.np_(g["parent"])
+    T = wl.nmax + 1
+    assert (gc.np_(g["n_nodes"]) == wl.nmax).all()
+    mask = gc.np_(g["mask"]).view(np.uint32)
+    pos = gc.np_(g["position_ids"])
+    parents = [[int(p) for p in parent[s]] for s in range(2)]
+    run_case(2, T, 8, 2, 512, [333, 17], parents, seed=11, mask_pos=(mask, pos))
