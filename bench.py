@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="main", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--cost", default="a100", choices=["a100", "mi355x", "calibrated"],
+                    help="verify-latency table of the online workloads: the roofline with the "
+                         "pages' GPU's constants (default), MI355X's published ones, or the "
+                         "constants fitted to this verifier's measured runtimes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the warm-input, accept and streaming-ceiling timings "
@@ -229,7 +233,12 @@ def main():
     bufs = [synth.make_logits(wl, device=dev, seed=wl.seed + i) for i in range(nbuf)]
     cost = None
     if wl.online:
-        c, _ = synth.make_cost_table(wl.B, wl.nmax, seed=wl.seed, **synth.LATENCY_A100)
+        if args.cost == "calibrated":
+            from block_diffusion_tree_amd import calibrate
+            c, _ = calibrate.calibrated_cost_table(wl.B, wl.nmax, seed=wl.seed)
+        else:
+            consts = synth.LATENCY_A100 if args.cost == "a100" else synth.LATENCY_MI355X
+            c, _ = synth.make_cost_table(wl.B, wl.nmax, seed=wl.seed, **consts)
         cost = torch.from_numpy(c).to(dev)
     ws = binding.Workspace(dev)
     if mixture:
@@ -319,7 +328,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}",
-                   "logits_dtype": wl.dtype, "rotating_buffers": nbuf},
+                   "logits_dtype": wl.dtype, "rotating_buffers": nbuf,
+                   **({"cost_table": args.cost} if wl.online else {})},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": ("build_trees_kernel (mixture mode) + mixture_kernel: the two launches "
@@ -332,6 +342,10 @@ def main():
                      "launch_us_p10": float(np.percentile(launch_ms, 10)) * 1e3,
                      "launch_us_p90": float(np.percentile(launch_ms, 90)) * 1e3},
     }
+    if wl.online:
+        nst = outs[0]["n_nodes"].cpu().numpy()
+        line["n_star"] = {"min": int(nst.min()), "p50": float(np.median(nst)),
+                          "max": int(nst.max()), "mean": float(nst.mean())}
     ceil = extras.get("ceiling")
     if ceil:
         line["roofline"]["ceiling"] = {

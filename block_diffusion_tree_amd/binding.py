@@ -381,8 +381,8 @@ def _vlib():
         L.bastion_tree_attention_workspace_bytes.restype = SZ
         L.bastion_tree_attention_workspace_bytes.argtypes = [I32] * 5
         L.bastion_tree_attention.restype = I32
-        L.bastion_tree_attention.argtypes = [P, I64, I32, I32, I32, I32, I32, P, P, I32, P, P, P,
-                                             I32, P, P, P, SZ, P]
+        L.bastion_tree_attention.argtypes = [P, I64, I32, I32, I32, I32, I32, P, P, I32, P, I32, P,
+                                             P, I32, P, P, P, SZ, P]
         _verify_lib = L
     return _verify_lib
 
@@ -399,12 +399,14 @@ def rope_inv_freq(theta: float = 1.0e6, head_dim: int = 128, device="cuda"):
 
 
 def tree_attention(qkv, S: int, T: int, Hq: int, Hkv: int, k_cache, v_cache, ctx_len,
-                   position_ids, mask, inv_freq, out=None, ws=None):
+                   position_ids, mask, inv_freq, out=None, ws=None, max_ctx: int = -1):
     """bastion_tree_attention: qkv [S*T, >= (Hq+2Hkv)*128] bf16 rows (unit
     stride over columns), k_cache [S, Hkv, Lmax, 128] and v_cache
-    [S, Hkv, 128, Lmax] bf16 (the tree tokens are written into them),
+    [S, Hkv, Lmax/32, 128, 32] bf16 (32-slot tiles; the tree tokens are
+    written into both),
     ctx_len [S] int32, position_ids [S, T] int32, mask [S, T, W] 32-bit words,
-    inv_freq [64] float32.  Returns out [S*T, Hq*128] bf16."""
+    inv_freq [64] float32; max_ctx a host bound of ctx_len (-1: the cache's).
+    Returns out [S*T, Hq*128] bf16."""
     D = 128
     dev = qkv.device
     if qkv.dim() != 2 or qkv.stride(1) != 1 or qkv.size(0) != S * T:
@@ -416,7 +418,7 @@ def tree_attention(qkv, S: int, T: int, Hq: int, Hkv: int, k_cache, v_cache, ctx
     Lmax = k_cache.size(2)
     W = (T + 31) // 32
     _need(k_cache, "k_cache", torch.bfloat16, (S, Hkv, Lmax, D), dev)
-    _need(v_cache, "v_cache", torch.bfloat16, (S, Hkv, D, Lmax), dev)
+    _need(v_cache, "v_cache", torch.bfloat16, (S, Hkv, Lmax // 32, D, 32), dev)
     _need(ctx_len, "ctx_len", torch.int32, (S,), dev)
     _need(position_ids, "position_ids", torch.int32, (S, T), dev)
     if mask.dtype not in (torch.int32, torch.uint32):
@@ -440,7 +442,8 @@ def tree_attention(qkv, S: int, T: int, Hq: int, Hkv: int, k_cache, v_cache, ctx
     if ws.numel() < need:
         raise ValueError(f"workspace needs {need} bytes")
     _check(L.bastion_tree_attention(_ptr(qkv), qkv.stride(0), S, T, Hq, Hkv, D, _ptr(k_cache),
-                                    _ptr(v_cache), Lmax, _ptr(ctx_len), _ptr(position_ids),
+                                    _ptr(v_cache), Lmax, _ptr(ctx_len), int(max_ctx),
+                                    _ptr(position_ids),
                                     _ptr(mask), W, _ptr(inv_freq), _ptr(out), _ptr(ws), ws.numel(),
                                     _stream()), "bastion_tree_attention")
     return out

@@ -11,16 +11,19 @@
 //   1. append: rotary position embedding of the tree tokens' q and k at
 //      their position ids (pos_base + depth), rounded to bf16; k and v go
 //      into the cache, q into a scratch laid out for the attention kernel;
-//   2. attention: per (64 query rows, KV head, key split), four waves of 16
-//      query rows each.  S^T = K Q^T and O^T += V^T P^T on MFMA
+//   2. attention: per (128 query rows, KV head, key split of 128 keys),
+//      eight waves of 16 query rows each; each 32-key step's K and V tiles
+//      are loaded once into LDS for the block (double-buffered: the next
+//      step's loads are in flight during this step).  S^T = K Q^T and O^T += V^T P^T on MFMA
 //      (v_mfma_f32_16x16x32_bf16): the S^T tile leaves each lane holding
 //      eight scores of one query row, which is exactly the B operand P^T of
 //      the second product, so the probabilities never leave registers.
 //      Online softmax (running max and sum per row) in float32;
 //   3. combine: the key splits' partial results, merged by their maxima.
 // Layouts: K cache [S][Hkv][Lmax][D] (a key's dims contiguous, the A operand
-// of S^T); V cache [S][Hkv][D][Lmax] (a dim's keys contiguous, the A operand
-// of O^T).
+// of S^T); V cache [S][Hkv][Lmax/32][D][32], tiles of 32 keys with a dim's
+// keys contiguous (the A operand of O^T), so that one 32-key step reads one
+// contiguous 8 KiB tile.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,30 +39,37 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kD = 128;           // head dim
 constexpr int kHalf = kD / 2;     // rotary pairs (d, d + 64)
 constexpr int kRowsPerWave = 16;  // one MFMA tile of query rows
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
 constexpr int kKeyStep = 32;      // keys per O^T MFMA step (two S^T tiles)
-constexpr int kSplitKeys = 256;   // keys per split
+constexpr int kSplitKeys = 128;   // keys per split
 
 struct AttnArgs {
     const __bf16 *qkv;        // [S*T][*] rows of the q/k/v projection
     int64_t qkv_stride;       // elements per row
     int S, T, Hq, Hkv, G, Lmax, W, rows, rows_pad, splits;
-    __bf16 *kc, *vc;          // caches
+    int ctx_cap;              // contexts are clamped to [0, ctx_cap]
+    __bf16 *kc, *vc;          // caches (vc in 32-key tiles)
     const int32_t *ctx;       // [S]
     const int32_t *pos;       // [S][T]
     const uint32_t *mask;     // [S][T][W]
     const float *inv_freq;    // [kHalf]
-    __bf16 *qs;               // [S][Hkv][rows_pad][kD] rotated q, zero padded
+    __bf16 *qs;               // [S][Hkv][rows_pad][kD] rotated q (rows past rows unused)
     float *opart;             // [splits][S][Hkv][rows_pad][kD]
     float *ml;                // [splits][S][Hkv][rows_pad][2]
     __bf16 *out;              // [S*T][Hq * kD]
     float scale_log2;         // log2(e) / sqrt(kD)
 };
 
-// cached tokens of sequence s, clamped so that the tree fits the cache
+// cached tokens of sequence s, clamped to the launch's bound (at most
+// Lmax - T, so that the tree fits the cache)
 __device__ __forceinline__ int ctx_of(const AttnArgs &A, int s) {
-    return min(max(A.ctx[s], 0), A.Lmax - A.T);
+    return min(max(A.ctx[s], 0), A.ctx_cap);
+}
+
+// element offset of the V-cache tile holding `key` of (s, h)
+__device__ __forceinline__ int64_t vtile(const AttnArgs &A, int s, int h, int key) {
+    return ((int64_t(s) * A.Hkv + h) * (A.Lmax / 32) + (key >> 5)) * (kD * 32);
 }
 
 // ---- 1. append ------------------------------------------------------------
@@ -98,15 +108,8 @@ __global__ __launch_bounds__(256) void append_kernel(AttnArgs A) {
     const __bf16 *vsrc = row + (A.Hq + A.Hkv) * kD;
     for (int e = threadIdx.x; e < A.Hkv * kD; e += blockDim.x) {
         const int h = e / kD, d = e - h * kD;
-        A.vc[((int64_t(s) * A.Hkv + h) * kD + d) * A.Lmax + (ctx + t)] = vsrc[h * kD + d];
-    }
-    // padding rows of the q scratch (after the last token's rows) are zero
-    if (t == A.T - 1) {
-        const int pad = A.rows_pad - A.rows;
-        for (int e = threadIdx.x; e < A.Hkv * pad * kD; e += blockDim.x) {
-            const int h = e / (pad * kD), r = (e / kD) % pad, d = e % kD;
-            A.qs[((int64_t(s) * A.Hkv + h) * A.rows_pad + A.rows + r) * kD + d] = __bf16(0.0f);
-        }
+        const int key = ctx + t;
+        A.vc[vtile(A, s, h, key) + d * 32 + (key & 31)] = vsrc[h * kD + d];
     }
 }
 
@@ -115,109 +118,163 @@ __device__ __forceinline__ float xor16_max(float v) {
     return fmaxf(v, __shfl_xor(v, 16));
 }
 
+// One 32-key step's tiles in LDS, shared by the block's waves: K as
+// [key][dim] (rows padded by 16 bytes), V as [dim][key] (rows padded by 16
+// bytes); double-buffered.
+constexpr int kKPad = kD + 8, kVPad = kKeyStep + 8;
+
+struct StepRegs {
+    bf16x8 k, v;   // this thread's share of a step's tiles (16 bytes of each)
+};
+
+constexpr int kSteps = kSplitKeys / kKeyStep;   // steps of one split
+
+// Thread x of the block loads 16 bytes of the K tile (key x / 16, dims
+// 8 (x % 16) ..) and 16 bytes of the V tile (dim x / 4, keys 8 (x % 4) ..)
+// of the step at kb.  Rows and tiles past the cache are clamped into it; the
+// contents of slots past the sequence do not matter (their scores are
+// masked, their v zeroed when stored).  The addresses do not depend on the
+// sequence's context, so these loads go out with the block's first ones.
+__device__ __forceinline__ StepRegs load_step(const __bf16 *kbase, const __bf16 *vbase, int kb,
+                                              int Lmax) {
+    const int x = threadIdx.x;
+    StepRegs R;
+    const int key = min(kb + (x >> 4), Lmax - 1);
+    R.k = *reinterpret_cast<const bf16x8 *>(kbase + int64_t(key) * kD + 8 * (x & 15));
+    const int tile = min(kb, Lmax - 32) >> 5;
+    R.v = *reinterpret_cast<const bf16x8 *>(vbase + int64_t(tile) * (kD * 32) + (x >> 2) * 32 +
+                                            8 * (x & 3));
+    return R;
+}
+
+// The step's tiles into LDS; v of keys at or past k1 set to zero (a slot
+// past the sequence may hold anything, NaN included).
+__device__ __forceinline__ void store_step(__bf16 (*ks)[kKPad], __bf16 (*vs)[kVPad], StepRegs R,
+                                           int kb, int k1) {
+    const int x = threadIdx.x;
+    const int k8 = 8 * (x & 3);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) R.v[e] = kb + k8 + e < k1 ? R.v[e] : __bf16(0.0f);
+    *reinterpret_cast<bf16x8 *>(&ks[x >> 4][8 * (x & 15)]) = R.k;
+    *reinterpret_cast<bf16x8 *>(&vs[x >> 2][k8]) = R.v;
+}
+
 __global__ __launch_bounds__(kWaves * 64) void attention_kernel(AttnArgs A) {
+    static_assert(kWaves * 64 == 32 * (kD / 8) && kWaves * 64 == kD * 4, "one load per thread");
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int h = blockIdx.y;
     const int s = blockIdx.z / A.splits, c = blockIdx.z - s * A.splits;
-    const int row0 = blockIdx.x * kRowsPerBlock + w * kRowsPerWave;
-    if (row0 >= A.rows) return;   // no barrier in this kernel: idle waves leave
+    const int k0 = c * kSplitKeys;
+    const int64_t hs = int64_t(s) * A.Hkv + h;
+    const __bf16 *kbase = A.kc + hs * A.Lmax * kD;
+    const __bf16 *vbase = A.vc + hs * int64_t(A.Lmax) * kD;   // the head's first tile
+    // every step's tiles of the split, issued first (one round trip for all)
+    StepRegs R[kSteps];
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) R[i] = load_step(kbase, vbase, k0 + i * kKeyStep, A.Lmax);
     const int ctx = ctx_of(A, s);
     const int L = ctx + A.T;
-    const int k0 = c * kSplitKeys;
+    if (k0 >= L) return;          // a split past this sequence's keys (whole block)
     const int k1 = min(L, k0 + kSplitKeys);
+    const int row0 = blockIdx.x * kRowsPerBlock + w * kRowsPerWave;
+    const bool active = row0 < A.rows;   // idle waves still load and synchronise
     const int r16 = lane & 15, g4 = lane >> 4;
     const int myrow = row0 + r16;
-    const int tok = min(myrow, A.rows - 1) / A.G;   // padding rows: any valid token
-    const int64_t hs = int64_t(s) * A.Hkv + h;
+    const int qr = min(myrow, A.rows - 1);   // rows past the last read a real one
+    const int tok = qr / A.G;
 
+    __shared__ __align__(16) __bf16 ks[2][kKeyStep][kKPad];
+    __shared__ __align__(16) __bf16 vs[2][kD][kVPad];
+    // the ancestor-mask rows of the wave's 16 query rows: the per-step bit
+    // lookups wait on LDS only, never on the next step's global loads
+    __shared__ uint32_t smask[kWaves][kRowsPerWave][32];
+    {
+        const uint32_t *mrow = A.mask + (int64_t(s) * A.T + tok) * A.W;
+        for (int x = g4; x < A.W; x += 4) smask[w][r16][x] = mrow[x];
+    }
     // Q^T, the B operand of S^T = K Q^T: lane (r16, g4) holds dims
     // 32 st + 8 g4 .. + 7 of its row
     bf16x8 qv[4];
-    const __bf16 *qrow = A.qs + (hs * A.rows_pad + myrow) * kD;
+    const __bf16 *qrow = A.qs + (hs * A.rows_pad + qr) * kD;
 #pragma unroll
     for (int st = 0; st < 4; ++st) qv[st] = *reinterpret_cast<const bf16x8 *>(qrow + 32 * st + 8 * g4);
 
-    const __bf16 *kbase = A.kc + hs * A.Lmax * kD;
-    const __bf16 *vbase = A.vc + hs * kD * A.Lmax;
-    const uint32_t *mrow = A.mask + (int64_t(s) * A.T + tok) * A.W;
+    store_step(ks[0], vs[0], R[0], k0, k1);
+    __syncthreads();
+    const uint32_t *mrow = smask[w][r16];
     float m = -INFINITY, lsum = 0.0f;
     f32x4 o[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int kb = k0; kb < k1; kb += kKeyStep) {
-        // two S^T tiles of 16 keys: key kb + r16 and kb + 16 + r16 (clamped:
-        // the score of a key past k1 is masked below)
-        const int ka = min(kb + r16, L - 1), kbb = min(kb + 16 + r16, L - 1);
-        f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(kbase + int64_t(ka) * kD + 32 * st + 8 * g4);
-            const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(kbase + int64_t(kbb) * kD + 32 * st + 8 * g4);
-            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qv[st], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qv[st], s1, 0, 0, 0);
-        }
-        // lane (r16, g4) now holds row r16's scores of keys kb + 4 g4 + r
-        // (s0) and kb + 16 + 4 g4 + r (s1), r = 0..3
-        float v[8];
-        const int kq = kb + 4 * g4;
+    for (int i = 0; i < kSteps; ++i) {
+        const int kb = k0 + i * kKeyStep;
+        if (kb >= k1) break;      // block-uniform
+        const int buf = i & 1;
+        if (active) {
+            f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int kk = kq + (r < 4 ? r : 12 + r);
-            const float sc = (r < 4 ? s0[r] : s1[r - 4]) * A.scale_log2;
-            bool vis = kk < k1;
-            if (vis && kk >= ctx) {
-                const int j = kk - ctx;
-                vis = (mrow[j >> 5] >> (j & 31)) & 1u;
+            for (int st = 0; st < 4; ++st) {
+                const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(&ks[buf][r16][32 * st + 8 * g4]);
+                const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(&ks[buf][16 + r16][32 * st + 8 * g4]);
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qv[st], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qv[st], s1, 0, 0, 0);
             }
-            v[r] = vis ? sc : -INFINITY;
-        }
-        float tmax = v[0];
+            // lane (r16, g4) now holds row r16's scores of keys kb + 4 g4 + r
+            // (s0) and kb + 16 + 4 g4 + r (s1), r = 0..3
+            float v[8];
+            const int kq = kb + 4 * g4;
 #pragma unroll
-        for (int r = 1; r < 8; ++r) tmax = fmaxf(tmax, v[r]);
-        tmax = xor16_max(tmax);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float mn = fmaxf(m, tmax);
-        const bool live = mn > -INFINITY;
-        const float alpha = live ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
-        bf16x8 pb;
-        float ps = 0.0f;
+            for (int r = 0; r < 8; ++r) {
+                const int kk = kq + (r < 4 ? r : 12 + r);
+                const float sc = (r < 4 ? s0[r] : s1[r - 4]) * A.scale_log2;
+                const int j = min(max(kk - ctx, 0), A.T - 1);
+                const bool bit = (mrow[j >> 5] >> (j & 31)) & 1u;
+                const bool vis = kk < k1 && (kk < ctx || bit);
+                v[r] = vis ? sc : -INFINITY;
+            }
+            float tmax = v[0];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const float p = live ? __builtin_amdgcn_exp2f(v[r] - mn) : 0.0f;
-            ps += p;
-            pb[r] = __bf16(p);
-        }
-        lsum = lsum * alpha + ps;
-        m = mn;
-        // V^T, the A operand of O^T += V^T P^T: dim 16 j + r16, keys in the
-        // same order as the lane's scores (4 of each S^T tile); keys past k1
-        // are zero (a cache slot past L may hold anything)
-        const bool full = kq + 20 <= k1;
+            for (int r = 1; r < 8; ++r) tmax = fmaxf(tmax, v[r]);
+            tmax = xor16_max(tmax);
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const float mn = fmaxf(m, tmax);
+            const bool live = mn > -INFINITY;
+            const float alpha = live ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
+            bf16x8 pb;
+            float ps = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const __bf16 *vr = vbase + int64_t(16 * j + r16) * A.Lmax;
-            bf16x8 av;
-            if (full) {
-                const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(vr + kq);
-                const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(vr + kq + 16);
+            for (int r = 0; r < 8; ++r) {
+                const float p = live ? __builtin_amdgcn_exp2f(v[r] - mn) : 0.0f;
+                ps += p;
+                pb[r] = __bf16(p);
+            }
+            lsum = lsum * alpha + ps;
+            m = mn;
+            // V^T, the A operand of O^T += V^T P^T: dim 16 j + r16, keys in
+            // the order of the lane's scores (4 of each S^T tile)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const __bf16 *vr = &vs[buf][16 * j + r16][4 * g4];
+                const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(vr);
+                const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(vr + 16);
+                bf16x8 av;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     av[r] = lo[r];
                     av[4 + r] = hi[r];
                 }
-            } else {
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int kk = kq + (r < 4 ? r : 12 + r);
-                    av[r] = kk < k1 ? vr[kk] : __bf16(0.0f);
-                }
+                for (int r = 0; r < 4; ++r) o[j][r] *= alpha;
+                o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, o[j], 0, 0, 0);
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[j][r] *= alpha;
-            o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, o[j], 0, 0, 0);
         }
+        // every wave is done with the other buffer since the last barrier
+        if (i + 1 < kSteps) store_step(ks[buf ^ 1], vs[buf ^ 1], R[i + 1], kb + kKeyStep, k1);
+        __syncthreads();
     }
+    if (!active) return;
     // the row's sum over its four lanes
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
@@ -247,48 +304,68 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(AttnArgs A) {
 }
 
 // ---- 3. combine -----------------------------------------------------------
-// Thread per (s, h, row, 4 dims).
+// One wave per (s, h, row): lane l holds the partial maxima and sums of
+// splits l, l + 64, ..; the row's maximum and normaliser are wave
+// reductions; then lane l accumulates dims 2 l, 2 l + 1 over the splits,
+// eight partial rows in flight at a time.
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs A) {
-    const int64_t n = int64_t(A.S) * A.Hkv * A.rows * (kD / 4);
-    for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < n;
-         e += int64_t(gridDim.x) * blockDim.x) {
-        const int d4 = int(e % (kD / 4));
-        const int64_t r_all = e / (kD / 4);
-        const int row = int(r_all % A.rows);
-        const int64_t sh = r_all / A.rows;   // s * Hkv + h
-        float M = -INFINITY;
-        for (int c = 0; c < A.splits; ++c)
-            M = fmaxf(M, A.ml[2 * ((c * int64_t(A.S * A.Hkv) + sh) * A.rows_pad + row)]);
-        float den = 0.0f;
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int c = 0; c < A.splits; ++c) {
-            const int64_t prow = (c * int64_t(A.S * A.Hkv) + sh) * A.rows_pad + row;
-            const float mc = A.ml[2 * prow];
-            if (!(mc > -INFINITY)) continue;
-            const float f = __builtin_amdgcn_exp2f(mc - M);
-            den += f * A.ml[2 * prow + 1];
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(A.opart + prow * kD + 4 * d4);
+    const int lane = threadIdx.x & 63;
+    const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wid >= A.S * A.Hkv * A.rows) return;
+    const int sh = wid / A.rows, row = wid - sh * A.rows;   // sh = s * Hkv + h
+    const int s = sh / A.Hkv, h = sh - s * A.Hkv;
+    const int live = (ctx_of(A, s) + A.T + kSplitKeys - 1) / kSplitKeys;
+    const int64_t stride = int64_t(A.S) * A.Hkv * A.rows_pad;   // one split's rows
+    const int64_t base = int64_t(sh) * A.rows_pad + row;
+    float mc[2], lc[2];
+    float M = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] += f * v[r];
-        }
-        const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-        const int s = int(sh / A.Hkv), h = int(sh % A.Hkv);
-        const int t = row / A.G, g = row - t * A.G;
-        __bf16 *dst = A.out + (int64_t(s) * A.T + t) * (int64_t(A.Hq) * kD) + (h * A.G + g) * kD + 4 * d4;
-        bf16x4 ov;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ov[r] = __bf16(acc[r] * inv);
-        *reinterpret_cast<bf16x4 *>(dst) = ov;
+    for (int u = 0; u < 2; ++u) {   // live <= 128 splits (Lmax <= 16384)
+        const int c = lane + 64 * u;
+        mc[u] = c < live ? A.ml[2 * (c * stride + base)] : -INFINITY;
+        lc[u] = c < live ? A.ml[2 * (c * stride + base) + 1] : 0.0f;
+        M = fmaxf(M, mc[u]);
     }
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float f[2], den = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        f[u] = mc[u] > -INFINITY ? __builtin_amdgcn_exp2f(mc[u] - M) : 0.0f;
+        den += f[u] * lc[u];
+    }
+    for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
+    float a0 = 0.0f, a1 = 0.0f;
+    for (int c0 = 0; c0 < live; c0 += 8) {
+        float2 v[8];
+        float fw[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int c = min(c0 + u, live - 1);
+            v[u] = *reinterpret_cast<const float2 *>(A.opart + (c * stride + base) * kD + 2 * lane);
+            const float fc = __shfl(f[(c >> 6) & 1], c & 63);
+            fw[u] = c0 + u < live ? fc : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            a0 += fw[u] * v[u].x;
+            a1 += fw[u] * v[u].y;
+        }
+    }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    const int t = row / A.G, g = row - t * A.G;
+    __bf16 *dst = A.out + (int64_t(s) * A.T + t) * (int64_t(A.Hq) * kD) + (h * A.G + g) * kD;
+    dst[2 * lane] = __bf16(a0 * inv);
+    dst[2 * lane + 1] = __bf16(a1 * inv);
 }
 
-int splits_for(int Lmax) { return (Lmax + kSplitKeys - 1) / kSplitKeys; }
+int splits_for(int keys) { return (keys + kSplitKeys - 1) / kSplitKeys; }
 
 int pad_rows(int rows) { return (rows + kRowsPerBlock - 1) / kRowsPerBlock * kRowsPerBlock; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// workspace: rotated q, partial outputs, partial (max, sum)
+// workspace: rotated q, partial outputs, partial (max, sum); sized for the
+// largest launch (contexts up to Lmax - T)
 void ws_layout(int S, int T, int Hq, int Hkv, int Lmax, size_t &oq, size_t &oo, size_t &om,
                size_t &total) {
     const int G = Hq / Hkv;
@@ -316,16 +393,18 @@ size_t bastion_tree_attention_workspace_bytes(int32_t S, int32_t T, int32_t Hq, 
 
 int32_t bastion_tree_attention(const void *qkv, int64_t qkv_row_stride, int32_t S, int32_t T,
                                int32_t Hq, int32_t Hkv, int32_t D, void *k_cache, void *v_cache,
-                               int32_t Lmax, const int32_t *ctx_len, const int32_t *position_ids,
-                               const uint32_t *mask, int32_t W, const float *inv_freq, void *out,
-                               void *ws, size_t ws_bytes, void *stream) {
+                               int32_t Lmax, const int32_t *ctx_len, int32_t max_ctx,
+                               const int32_t *position_ids, const uint32_t *mask, int32_t W,
+                               const float *inv_freq, void *out, void *ws, size_t ws_bytes,
+                               void *stream) {
     if (!qkv || !k_cache || !v_cache || !ctx_len || !position_ids || !mask || !inv_freq || !out)
         return BASTION_EINVAL;
     if (S < 1 || T < 1 || T > 1024 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0) return BASTION_EINVAL;
+    if (int64_t(S) * Hq * T >= (int64_t(1) << 31) || Lmax > 16384) return BASTION_EUNSUPPORTED;
     const int G = Hq / Hkv;
     if (G > 16 || 16 % G != 0) return BASTION_EUNSUPPORTED;
     if (D != kD) return BASTION_EUNSUPPORTED;
-    if (W != (T + 31) / 32 || Lmax < T || Lmax % 8 != 0) return BASTION_EINVAL;
+    if (W != (T + 31) / 32 || Lmax < T || Lmax % 32 != 0) return BASTION_EINVAL;
     if (qkv_row_stride < int64_t(Hq + 2 * Hkv) * kD || qkv_row_stride % 8 != 0)
         return BASTION_EINVAL;
     if (!aligned(qkv, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
@@ -339,7 +418,8 @@ int32_t bastion_tree_attention(const void *qkv, int64_t qkv_row_stride, int32_t 
     A.S = S; A.T = T; A.Hq = Hq; A.Hkv = Hkv; A.G = G; A.Lmax = Lmax; A.W = W;
     A.rows = T * G;
     A.rows_pad = pad_rows(A.rows);
-    A.splits = splits_for(Lmax);
+    A.ctx_cap = (max_ctx >= 0 && max_ctx < Lmax - T) ? max_ctx : Lmax - T;
+    A.splits = splits_for(A.ctx_cap + T);
     A.kc = static_cast<__bf16 *>(k_cache);
     A.vc = static_cast<__bf16 *>(v_cache);
     A.ctx = ctx_len;
@@ -358,10 +438,8 @@ int32_t bastion_tree_attention(const void *qkv, int64_t qkv_row_stride, int32_t 
                                               unsigned(S * A.splits)),
                        dim3(kWaves * 64), 0, st, A);
     if (A.splits > 1) {
-        const int64_t n = int64_t(S) * Hkv * A.rows * (kD / 4);
-        const int64_t blocks = (n + 255) / 256;
-        hipLaunchKernelGGL(combine_kernel, dim3(unsigned(blocks < 4096 ? blocks : 4096)), dim3(256),
-                           0, st, A);
+        const int64_t waves = int64_t(S) * Hkv * A.rows;
+        hipLaunchKernelGGL(combine_kernel, dim3(unsigned((waves + 3) / 4)), dim3(256), 0, st, A);
     }
     return hipGetLastError() == hipSuccess ? BASTION_OK : BASTION_EHIP;
 }

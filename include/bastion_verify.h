@@ -40,10 +40,15 @@ size_t bastion_tree_attention_workspace_bytes(int32_t S, int32_t T, int32_t Hq, 
  *   sequence s, qkv_row_stride elements apart (>= (Hq + 2 Hkv) D, a multiple
  *   of 8); q head h at columns [h D, (h+1) D), k head h at
  *   [(Hq + h) D, ...), v head h at [(Hq + Hkv + h) D, ...).
- * k_cache: bf16 [S][Hkv][Lmax][D]; v_cache: bf16 [S][Hkv][D][Lmax].  Slots
+ * k_cache: bf16 [S][Hkv][Lmax][D]; v_cache: bf16 [S][Hkv][Lmax/32][D][32]
+ *   (tiles of 32 slots, a dim's 32 slots contiguous: value dim d of slot j
+ *   at [s][h][j/32][d][j%32]).  Slots
  *   0 .. ctx-1 hold the cached tokens (k already rotated at its position);
  *   the call writes the tree tokens' rotated k and their v into slots
- *   ctx .. ctx+T-1, where ctx = ctx_len[s] clamped to [0, Lmax - T].
+ *   ctx .. ctx+T-1, where ctx = ctx_len[s] clamped to [0, cap] with
+ *   cap = max_ctx if 0 <= max_ctx < Lmax - T, else Lmax - T.  max_ctx is the
+ *   caller's host-side bound of the contexts: it sizes the launch (key
+ *   splits of 128 slots up to cap + T), so a tight bound saves blocks.
  * position_ids [S][T] int32 (bastion_build_trees' pos_base + depth with
  *   pos_base = ctx): each tree token's q and k are rotated at its position:
  *   the pair (x_d, x_{d+D/2}), d < D/2, by the float32 angle
@@ -56,16 +61,17 @@ size_t bastion_tree_attention_workspace_bytes(int32_t S, int32_t T, int32_t Hq, 
  *   q head h = kv_head * (Hq/Hkv) + g.  Scores and softmax in float32; the
  *   probabilities enter the value product rounded to bf16.
  * Limits: D = 128, Hq % Hkv == 0 with Hq/Hkv dividing 16, 1 <= T <= 1024,
- *   T <= Lmax, Lmax % 8 == 0; qkv, caches and out 16-byte aligned; ws
+ *   T <= Lmax <= 16384, Lmax % 32 == 0; qkv, caches and out 16-byte aligned; ws
  *   256-byte aligned with at least bastion_tree_attention_workspace_bytes.
- * Errors: EINVAL (pointers, sizes, strides, alignment), EUNSUPPORTED (D or
- *   the group size), EWORKSPACE.
+ * Errors: EINVAL (pointers, sizes, strides, alignment), EUNSUPPORTED (D,
+ *   the group size, or Lmax above 16384), EWORKSPACE.
  */
 int32_t bastion_tree_attention(const void *qkv, int64_t qkv_row_stride, int32_t S, int32_t T,
                                int32_t Hq, int32_t Hkv, int32_t D, void *k_cache, void *v_cache,
-                               int32_t Lmax, const int32_t *ctx_len, const int32_t *position_ids,
-                               const uint32_t *mask, int32_t W, const float *inv_freq, void *out,
-                               void *ws, size_t ws_bytes, void *stream);
+                               int32_t Lmax, const int32_t *ctx_len, int32_t max_ctx,
+                               const int32_t *position_ids, const uint32_t *mask, int32_t W,
+                               const float *inv_freq, void *out, void *ws, size_t ws_bytes,
+                               void *stream);
 
 #ifdef __cplusplus
 }

@@ -53,11 +53,16 @@ def test_main_workload_full_parity():
 
 
 def cost_table(B, nmax, seed, consts):
-    c, _ = synth.make_cost_table(B, nmax, seed=seed, **consts)
+    if consts == "calibrated":
+        # the verify-latency roofline fitted on an MI355X
+        from block_diffusion_tree_amd import calibrate
+        c, _ = calibrate.calibrated_cost_table(B, nmax, seed)
+    else:
+        c, _ = synth.make_cost_table(B, nmax, seed=seed, **consts)
     return torch.from_numpy(c).to("cuda")
 
 
-@pytest.mark.parametrize("consts", [synth.LATENCY_A100, synth.LATENCY_MI355X])
+@pytest.mark.parametrize("consts", [synth.LATENCY_A100, synth.LATENCY_MI355X, "calibrated"])
 def test_online_budget_sweep_slice(consts):
     wl = synth.scaled(synth.WORKLOADS["sweep"], B=16)
     x = gc.device_logits(wl)

@@ -25,25 +25,30 @@ def to_dev(a, dtype):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dtype).to("cuda")
 
 
-def run_case(S, T, Hq, Hkv, Lmax, ctx, parents, seed, poison=True, mask_pos=None):
+def run_case(S, T, Hq, Hkv, Lmax, ctx, parents, seed, poison=True, mask_pos=None, max_ctx=-1):
     gc.require_gpu()
     rng = np.random.default_rng(seed)
     qkv, kc, vc, ctxa, pos, mask, inv = make_case(rng, S, T, Hq, Hkv, Lmax, ctx, parents)
     if mask_pos is not None:
         mask, pos = mask_pos
-    ref, kc_ref, vc_ref = vo.tree_attention(qkv, S, T, Hq, Hkv, 128, kc, vc, ctxa, pos, mask, inv)
+    # the reference sees the contexts the launch bound leaves
+    ctx_ref = ctxa if max_ctx < 0 else np.minimum(ctxa, max_ctx).astype(np.int32)
+    ref, kc_ref, vc_ref = vo.tree_attention(qkv, S, T, Hq, Hkv, 128, kc, vc, ctx_ref, pos, mask,
+                                            inv)
     kcd = to_dev(kc, torch.bfloat16)
     vcd = to_dev(vc, torch.bfloat16)
     if poison:
         # slots past each sequence's keys hold NaN: nothing may read them
         for s in range(S):
-            end = min(max(int(ctx[s]), 0), Lmax - T) + T
+            end = min(max(int(ctx_ref[s]), 0), Lmax - T) + T
             kcd[s, :, end:, :] = float("nan")
             vcd[s, :, :, end:] = float("nan")
+    # the library's v cache is tiled: [S, Hkv, Lmax/32, D, 32]
+    vcd = vcd.view(S, Hkv, 128, Lmax // 32, 32).permute(0, 1, 3, 2, 4).contiguous()
     out = binding.tree_attention(to_dev(qkv, torch.bfloat16), S, T, Hq, Hkv, kcd, vcd,
                                  to_dev(ctxa, torch.int32), to_dev(pos, torch.int32),
                                  to_dev(mask.view(np.int32), torch.int32),
-                                 to_dev(inv, torch.float32))
+                                 to_dev(inv, torch.float32), max_ctx=max_ctx)
     torch.cuda.synchronize()
     got = out.double().cpu().numpy()
     vmax = np.abs(qkv[:, (Hq + Hkv) * 128:(Hq + 2 * Hkv) * 128]).max()
@@ -54,9 +59,9 @@ def run_case(S, T, Hq, Hkv, Lmax, ctx, parents, seed, poison=True, mask_pos=None
     assert (err <= bound).all(), f"max err {err.max()} (bound at worst {bound[err > bound].min()})"
     # caches: v copied exactly, rotated k within one bf16 step
     kg = kcd.double().cpu().numpy()
-    vg = vcd.double().cpu().numpy()
+    vg = vcd.permute(0, 1, 3, 2, 4).reshape(S, Hkv, 128, Lmax).double().cpu().numpy()
     for s in range(S):
-        c = min(max(int(ctx[s]), 0), Lmax - T)
+        c = min(max(int(ctx_ref[s]), 0), Lmax - T)
         assert np.array_equal(vg[s, :, :, :c + T], vc_ref[s, :, :, :c + T])
         dk = np.abs(kg[s, :, c:c + T, :] - kc_ref[s, :, c:c + T, :])
         ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(kc_ref[s, :, c:c + T, :]), 1e-30))) - 7)
@@ -71,7 +76,7 @@ def random_parents(rng, S, T):
 
 @pytest.mark.parametrize("S,T,Hq,Hkv,Lmax,ctx", [
     (2, 9, 8, 2, 64, [5, 0]),            # one key split: output written directly
-    (1, 65, 32, 8, 1024, [700]),         # Qwen3-8B heads, N = 64, four splits combined
+    (1, 65, 32, 8, 1024, [700]),         # Qwen3-8B heads, N = 64, splits combined
     (3, 33, 16, 16, 512, [0, 300, 40]),  # no grouping
     (1, 129, 16, 1, 256, [100]),         # one KV head for 16 query heads
     (2, 17, 4, 2, 96, [90, 200]),        # contexts past the cache are clamped
@@ -79,6 +84,14 @@ def random_parents(rng, S, T):
 def test_tree_attention_matches_reference(S, T, Hq, Hkv, Lmax, ctx):
     rng = np.random.default_rng(T)
     run_case(S, T, Hq, Hkv, Lmax, ctx, random_parents(rng, S, T), seed=T + S)
+
+
+def test_tree_attention_launch_bound():
+    """A host bound of the contexts sizes the launch; contexts above it are
+    clamped to it (here 300 of 700 cached tokens are used)."""
+    rng = np.random.default_rng(8)
+    run_case(2, 33, 8, 2, 1024, [700, 120], random_parents(rng, 2, 33), seed=8, max_ctx=300)
+    run_case(2, 33, 8, 2, 1024, [700, 120], random_parents(rng, 2, 33), seed=9, max_ctx=700)
 
 
 def test_tree_attention_large_tree():
