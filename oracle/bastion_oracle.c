@@ -512,6 +512,99 @@ void oracle_mixture(const void *branch_logits, int dtype, const float *prior_log
     free(p);
 }
 
+/* ------------------------------------------------------------------------
+ * Candidates from the mixture marginal  [D-M1] with [B-M1].
+ * The latent mixture's position-i marginal is
+ *   m_i(x) = sum_z w_z p_{z,i}(x),   w = softmax(prior logits),
+ * p_{z,i} the full-vocabulary softmax of branch row (z, i).  The candidates
+ * of position i are the k tokens ranked first by (m desc, token asc); each
+ * comes with m and with p_{z,i}(x) for every branch z (the mixture tree's
+ * per-branch factors).  float64 throughout.
+ * Outputs: prior_w [B,K], marg_ids [B,b,k], marg_p [B,b,k],
+ * cand_p [B,b,k,K], row_status [B,K,b].
+ * ------------------------------------------------------------------------ */
+void oracle_mixture_marginal(const void *branch_logits, int dtype,
+                             const float *prior_logits, int B, int K, int b, int V,
+                             int64_t row_stride, int k, double *prior_w,
+                             int32_t *marg_ids, double *marg_p, double *cand_p,
+                             int32_t *row_status)
+{
+    int64_t nrows = (int64_t)B * K * b;
+    double *row_max = (double *)malloc(sizeof(double) * (size_t)nrows);
+    double *row_sum = (double *)malloc(sizeof(double) * (size_t)nrows);
+    int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)nrows);
+    double *p1 = (double *)malloc(sizeof(double) * (size_t)nrows);
+    oracle_softmax_topk(branch_logits, dtype, nrows, V, row_stride, 1, row_max,
+                        row_sum, ids, p1, row_status);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int qi = 0; qi < B * b; ++qi) {
+        int q = qi / b, i = qi - q * b;
+        double pm = -INFINITY, ps = 0.0;
+        for (int z = 0; z < K; ++z)
+            if ((double)prior_logits[q * K + z] > pm)
+                pm = (double)prior_logits[q * K + z];
+        for (int z = 0; z < K; ++z)
+            ps += exp((double)prior_logits[q * K + z] - pm);
+        if (i == 0)
+            for (int z = 0; z < K; ++z)
+                prior_w[q * K + z] = exp((double)prior_logits[q * K + z] - pm) / ps;
+        int bad = 0;
+        for (int z = 0; z < K; ++z)
+            for (int j = 0; j < b; ++j)
+                if (row_status[((int64_t)q * K + z) * b + j] != ORACLE_OK)
+                    bad = 1;
+        int32_t *oid = marg_ids + (int64_t)qi * k;
+        double *op = marg_p + (int64_t)qi * k;
+        double *oc = cand_p + (int64_t)qi * k * K;
+        if (bad) {
+            for (int j = 0; j < k; ++j) {
+                oid[j] = -1;
+                op[j] = 0.0;
+                for (int z = 0; z < K; ++z)
+                    oc[j * K + z] = 0.0;
+            }
+            continue;
+        }
+        /* the marginal of every token */
+        double *m = (double *)malloc(sizeof(double) * (size_t)V);
+        unsigned char *taken = (unsigned char *)calloc((size_t)V, 1);
+        for (int x = 0; x < V; ++x) {
+            double acc = 0.0;
+            for (int z = 0; z < K; ++z) {
+                int64_t row = ((int64_t)q * K + z) * b + i;
+                double w = exp((double)prior_logits[q * K + z] - pm) / ps;
+                acc += w * exp(logit_at(branch_logits, dtype, row * row_stride + x) - row_max[row]) /
+                       row_sum[row];
+            }
+            m[x] = acc;
+        }
+        /* k rounds of "take the best remaining token" */
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int x = 0; x < V; ++x) {
+                if (taken[x])
+                    continue;
+                if (best < 0 || m[x] > m[best])   /* ties keep the smaller id */
+                    best = x;
+            }
+            taken[best] = 1;
+            oid[j] = best;
+            op[j] = m[best];
+            for (int z = 0; z < K; ++z) {
+                int64_t row = ((int64_t)q * K + z) * b + i;
+                oc[j * K + z] = exp(logit_at(branch_logits, dtype, row * row_stride + best) -
+                                    row_max[row]) / row_sum[row];
+            }
+        }
+        free(m);
+        free(taken);
+    }
+    free(row_max);
+    free(row_sum);
+    free(ids);
+    free(p1);
+}
+
 /*
  * q_dep of arbitrary token sequences  [D-M1]:
  * seqs [B, n, b] -> out [B, n] = sum_z w_z prod_i p_{z,i}(seq_i).

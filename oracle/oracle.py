@@ -64,11 +64,12 @@ def _declare(L):
     L.oracle_mixture.argtypes = [P, I32, P, I32, I32, I32, I32, I64, I32,
                                  P, P, P, P, P, P, P]
     L.oracle_qdep_sequences.argtypes = [P, I32, P, I32, I32, I32, I32, I64, P, I32, P]
+    L.oracle_mixture_marginal.argtypes = [P, I32, P, I32, I32, I32, I32, I64, I32, P, P, P, P, P]
     L.oracle_mixture_tree.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32,
                                       P, P, P, P, P, P, P]
     for f in ("oracle_softmax_topk", "oracle_best_first", "oracle_budget_select",
               "oracle_tree_mask", "oracle_accept", "oracle_mixture",
-              "oracle_qdep_sequences", "oracle_mixture_tree"):
+              "oracle_qdep_sequences", "oracle_mixture_tree", "oracle_mixture_marginal"):
         getattr(L, f).restype = None
 
 
@@ -196,6 +197,22 @@ def mixture(branch_logits, prior_logits, k: int):
                          _p(out["chain_tokens"]), _p(out["qdep_chain"]),
                          _p(out["cand_count"]), _p(out["cand_tokens"]), _p(out["cand_p"]),
                          _p(out["row_status"]))
+    return out
+
+
+def mixture_marginal(branch_logits, prior_logits, k: int):
+    """Candidates by the mixture marginal: branch_logits [B,K,b,V] (float32 or
+    bf16 bits), prior [B,K] -> prior_w, marg_ids [B,b,k], marg_p [B,b,k],
+    cand_p [B,b,k,K], row_status [B,K,b]."""
+    a, dt = _raw_logits(branch_logits)
+    B, K, b, V = a.shape
+    pr = _c(prior_logits, np.float32)
+    out = dict(prior_w=np.empty((B, K), np.float64), marg_ids=np.empty((B, b, k), np.int32),
+               marg_p=np.empty((B, b, k), np.float64), cand_p=np.empty((B, b, k, K), np.float64),
+               row_status=np.empty((B, K, b), np.int32))
+    lib().oracle_mixture_marginal(_p(a), dt, _p(pr), B, K, b, V, V, k, _p(out["prior_w"]),
+                                  _p(out["marg_ids"]), _p(out["marg_p"]), _p(out["cand_p"]),
+                                  _p(out["row_status"]))
     return out
 
 

@@ -253,3 +253,68 @@ def test_qdep_random_branches_match_sequence_routine(oracle_mod):
             want = sum(w[zp] * np.prod([p[qq, zp, i, chain[i]] for i in range(b)])
                        for zp in range(K))
             assert m["qdep_chain"][qq, z] == pytest.approx(want, rel=1e-12)
+
+
+# ---- candidates from the mixture marginal -----------------------------------
+
+def numpy_marginal(x, prior):
+    """sum_z w_z softmax(row z) in float64 with numpy (an independent route)."""
+    xd = x.astype(np.float64)
+    p = np.exp(xd - xd.max(axis=-1, keepdims=True))
+    p /= p.sum(axis=-1, keepdims=True)                     # [B,K,b,V]
+    pr = prior.astype(np.float64)
+    w = np.exp(pr - pr.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)                      # [B,K]
+    return np.einsum("bz,bziv->biv", w, p), p, w
+
+
+def test_marginal_matches_numpy_and_lexsort(oracle_mod):
+    rng = np.random.default_rng(21)
+    B, K, b, V, k = 2, 3, 4, 50, 6
+    x = np.round(rand_branch_logits(rng, B, K, b, V) * 2) / 2   # ties in the logits
+    prior = rng.standard_normal((B, K)).astype(np.float32)
+    r = oracle_mod.mixture_marginal(x, prior, k)
+    m, p, w = numpy_marginal(x, prior)
+    assert np.allclose(r["prior_w"], w, rtol=1e-14)
+    for qq in range(B):
+        for i in range(b):
+            ids = np.arange(V)
+            # the ranking of numpy's marginal, rounded so that equal mixtures
+            # of tied logits compare equal
+            want = np.lexsort((ids, -np.round(m[qq, i], 12)))[:k]
+            assert r["marg_ids"][qq, i].tolist() == want.tolist()
+            assert np.allclose(r["marg_p"][qq, i], m[qq, i, want], rtol=1e-12)
+            assert np.allclose(r["cand_p"][qq, i], p[qq][:, i][:, want].T, rtol=1e-12)
+
+
+def test_marginal_sums_to_one_and_k1_is_the_plain_topk(oracle_mod):
+    rng = np.random.default_rng(22)
+    x = rand_branch_logits(rng, 2, 3, 2, 12)
+    prior = rng.standard_normal((2, 3)).astype(np.float32)
+    r = oracle_mod.mixture_marginal(x, prior, 12)           # k = V: every token
+    assert np.allclose(r["marg_p"].sum(axis=-1), 1.0, rtol=0, atol=1e-14)
+    # one branch: the marginal is that branch's softmax, its top-k the row's
+    one = rand_branch_logits(rng, 2, 1, 3, 40)
+    r1 = oracle_mod.mixture_marginal(one, np.zeros((2, 1), np.float32), 5)
+    sm = oracle_mod.softmax_topk(one[:, 0], k=5)
+    assert (r1["marg_ids"] == sm["topk_ids"]).all()
+    assert np.allclose(r1["marg_p"], sm["topk_p"], rtol=1e-13)
+
+
+def test_marginal_of_disjoint_one_hot_branches_is_the_prior(oracle_mod):
+    """Branch z puts all its mass on token t_z: m(t_z) = w_z, so the
+    candidates are the branches' tokens in prior order (then token order)."""
+    K, b, V = 4, 2, 30
+    x = np.full((1, K, b, V), -np.inf, np.float32)
+    toks = [[7, 3], [1, 9], [20, 2], [5, 11]]
+    for z in range(K):
+        for i in range(b):
+            x[0, z, i, toks[z][i]] = 0.5 * z
+    prior = np.array([[0.3, 1.2, -0.4, 1.2]], np.float32)   # branches 1 and 3 tie
+    r = oracle_mod.mixture_marginal(x, prior, 4)
+    w = np.exp(prior[0].astype(np.float64) - 1.2)
+    w /= w.sum()
+    for i in range(b):
+        order = sorted(range(K), key=lambda z: (-w[z], toks[z][i]))
+        assert r["marg_ids"][0, i].tolist() == [toks[z][i] for z in order]
+        assert np.allclose(r["marg_p"][0, i], [w[z] for z in order], rtol=1e-14)
