@@ -47,6 +47,10 @@ def parse():
                     help="verify-latency table of the online workloads: the roofline with the "
                          "pages' GPU's constants (default), MI355X's published ones, or the "
                          "constants fitted to this verifier's measured runtimes")
+    ap.add_argument("--candidates", default="union", choices=["union", "marginal"],
+                    help="mixture workload: candidates from the union of the branches' top-k "
+                         "(bastion_mixture_score) or the top-k of the mixture marginal "
+                         "(bastion_mixture_marginal, a second pass over the branch rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the warm-input, accept and streaming-ceiling timings "
@@ -157,6 +161,27 @@ def cpu_baseline_mixture(x, prior, wl, mout, n_queries, min_seconds=2.0, max_rep
                                      f"{reps1} passes, {dt1:.3f} s per pass"), ok
 
 
+def cpu_baseline_marginal(x, prior, wl, n_queries, min_seconds=2.0, max_reps=10):
+    """The CPU reference of the marginal rule (candidates and the mixture
+    tree) on the first n_queries queries, all host threads."""
+    from oracle import oracle
+    import numpy as np
+    xs = oracle.host_logits(x[:n_queries])
+    ps = prior[:n_queries].cpu().numpy()
+
+    def one():
+        m = oracle.mixture_marginal(xs, ps, wl.k)
+        cnt = np.full((n_queries, wl.b), wl.k, np.int32)
+        oracle.mixture_tree(m["prior_w"].astype(np.float32), cnt, m["marg_ids"],
+                            m["cand_p"].astype(np.float32), nmax=wl.nmax,
+                            row_status=m["row_status"])
+    dt, reps, _ = _timed(one, min_seconds, max_reps)
+    return dict(value=n_queries / dt, unit="trees/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"first {n_queries} of {wl.B} queries of the timed batch: float64 mixture "
+                       f"marginal over every token, its top-k, mixture tree; median of {reps} "
+                       f"passes, {dt:.3f} s per pass")
+
+
 def stream_ceiling(bufs, dev, reps=20):
     """The practical HBM read rate: a plain streaming-read kernel
     (libbastion_probe.so) over the same input buffers, rotating like the
@@ -241,9 +266,11 @@ def main():
             c, _ = synth.make_cost_table(wl.B, wl.nmax, seed=wl.seed, **consts)
         cost = torch.from_numpy(c).to(dev)
     ws = binding.Workspace(dev)
+    marginal = mixture and args.candidates == "marginal"
     if mixture:
         prior = synth.make_prior_logits(wl, device=dev)
-        mouts = [binding.alloc_mixture_out(wl.B, wl.K, wl.b, wl.k, dev) for _ in range(nbuf)]
+        alloc = binding.alloc_marginal_out if marginal else binding.alloc_mixture_out
+        mouts = [alloc(wl.B, wl.K, wl.b, wl.k, dev) for _ in range(nbuf)]
         outs = [binding.alloc_tree_out(wl.B, wl.b, wl.k, wl.nmax, dev, with_rows=False)
                 for _ in range(nbuf)]
     else:
@@ -253,8 +280,9 @@ def main():
     # caller looping over fixed buffers does the same), so that the host keeps
     # ahead of the GPU and the events time the GPU work
     if mixture:
-        calls = [binding.prepare_mixture_score(bufs[j], prior, k=wl.k, nmax=wl.nmax, out=mouts[j],
-                                               tree=outs[j], ws=ws)[2] for j in range(nbuf)]
+        prep = binding.prepare_mixture_marginal if marginal else binding.prepare_mixture_score
+        calls = [prep(bufs[j], prior, k=wl.k, nmax=wl.nmax, out=mouts[j], tree=outs[j], ws=ws)[2]
+                 for j in range(nbuf)]
     else:
         calls = [binding.prepare_build_trees(bufs[j], k=wl.k, nmax=wl.nmax, nmin=wl.nmin, cost=cost,
                                              out=outs[j], ws=ws)[1] for j in range(nbuf)]
@@ -304,7 +332,9 @@ def main():
         extras["ceiling"] = stream_ceiling(bufs, dev)
 
     ms_per_step = wall * 1e3 / args.steps
-    alg_bytes = wl.logit_bytes + out_bytes(outs[0])
+    # the marginal rule reads every branch logit twice: its ranking needs
+    # each row's normaliser first
+    alg_bytes = wl.logit_bytes * (2 if marginal else 1) + out_bytes(outs[0])
     if mixture:
         alg_bytes += out_bytes(mouts[0]) + prior.numel() * 4
     mean_ms = float(launch_ms.mean())
@@ -329,7 +359,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}",
                    "logits_dtype": wl.dtype, "rotating_buffers": nbuf,
-                   **({"cost_table": args.cost} if wl.online else {})},
+                   **({"cost_table": args.cost} if wl.online else {}),
+                   **({"candidates": args.candidates} if mixture else {})},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": ("build_trees_kernel (mixture mode) + mixture_kernel: the two launches "
@@ -342,6 +373,12 @@ def main():
                      "launch_us_p10": float(np.percentile(launch_ms, 10)) * 1e3,
                      "launch_us_p90": float(np.percentile(launch_ms, 90)) * 1e3},
     }
+    if mixture:
+        # A_hat of the emitted trees (the rules' expected committed tokens)
+        nn = outs[0]["n_nodes"].long()
+        ah = outs[0]["ahat"].gather(1, nn.view(-1, 1)).view(-1)
+        line["ahat_at_n"] = {"mean": float(ah.mean()), "min": float(ah.min()),
+                             "max": float(ah.max())}
     if wl.online:
         nst = outs[0]["n_nodes"].cpu().numpy()
         line["n_star"] = {"min": int(nst.min()), "p50": float(np.median(nst)),
@@ -370,7 +407,10 @@ def main():
         line["calib_copy_bytes"] = n
     if not args.no_cpu_baseline:
         from oracle import oracle
-        if mixture:
+        if marginal:
+            base = cpu_baseline_marginal(bufs[0], prior, wl, n_queries=2)
+            line["cpu_baseline"] = base
+        elif mixture:
             base, ok = cpu_baseline_mixture(bufs[0], prior, wl, mouts[0], n_queries=2)
             line["cpu_baseline"] = base
             line["parity_sample"] = {"queries": 2, "chain_tokens_exact": ok}

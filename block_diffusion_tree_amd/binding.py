@@ -44,6 +44,10 @@ class MixOut(C.Structure):
                                  "cand_tokens", "cand_q", "row_max", "row_sum")]
 
 
+class MargOut(C.Structure):
+    _fields_ = [(n, P) for n in ("prior_q", "row_max", "row_sum", "marg_ids", "marg_q", "cand_q")]
+
+
 def use_library(path: str):
     """Load `path` instead of libbastion.so (the stamped build of the same
     sources); must come before the first call."""
@@ -77,6 +81,9 @@ def lib():
         L.bastion_tree_mask.argtypes = [P, P, I32, I32, P, P, P, P]
         L.bastion_accept.restype = I32
         L.bastion_accept.argtypes = [P, P, P, I32, I32, I32, P, P, P, P, P]
+        L.bastion_mixture_marginal.restype = I32
+        L.bastion_mixture_marginal.argtypes = [P, I32, P, I32, I32, I32, I32, I64, I32, I32,
+                                               C.POINTER(MargOut), C.POINTER(TreeOut), P, SZ, P]
         L.bastion_set_tuning.restype = None
         L.bastion_set_tuning.argtypes = [I32, I32]
         L.bastion_mixture_score.restype = I32
@@ -521,3 +528,66 @@ def prepare_mixture_score(branch_logits, prior_logits, k: int, nmax: int, with_t
     """mixture_score with its arguments checked and marshalled once: returns
     (out, tree, call)."""
     return _mixture_call(branch_logits, prior_logits, k, nmax, with_tree, with_mask, out, tree, ws)
+
+
+def alloc_marginal_out(B, K, b, k, device):
+    f32 = dict(dtype=torch.float32, device=device)
+    return dict(prior_q=torch.empty((B, K), **f32), row_max=torch.empty((B, K, b), **f32),
+                row_sum=torch.empty((B, K, b), **f32),
+                marg_ids=torch.empty((B, b, k), dtype=torch.int32, device=device),
+                marg_q=torch.empty((B, b, k), **f32), cand_q=torch.empty((B, b, k, K), **f32))
+
+
+def _marginal_call(branch_logits, prior_logits, k, nmax, with_tree, with_mask, out, tree, ws):
+    _dev(branch_logits, "branch_logits")
+    x = branch_logits
+    if x.dim() != 4 or x.stride(3) != 1 or x.stride(1) != x.size(2) * x.stride(2) \
+            or x.stride(0) != x.size(1) * x.stride(1):
+        raise ValueError("branch_logits must be [B, K, b, V] with unit stride over V and rows packed")
+    B, K, b, V = x.shape
+    dt = _dtype_code(x)
+    _need(prior_logits, "prior_logits", torch.float32, (B, K), x.device)
+    if out is None:
+        out = alloc_marginal_out(B, K, b, k, x.device)
+    spec = dict(prior_q=(torch.float32, (B, K)), row_max=(torch.float32, (B, K, b)),
+                row_sum=(torch.float32, (B, K, b)), marg_ids=(torch.int32, (B, b, k)),
+                marg_q=(torch.float32, (B, b, k)), cand_q=(torch.float32, (B, b, k, K)))
+    for name, (tdt, shape) in spec.items():
+        _need(out[name], name, tdt, shape, x.device)
+    if with_tree and tree is None:
+        tree = alloc_tree_out(B, b, k, nmax, x.device, with_rows=False, with_mask=with_mask)
+    if not with_tree:
+        tree = None
+    if tree is not None:
+        _check_tree_out(tree, B, b, k, nmax, x.device, with_rows=False)
+    L = lib()
+    w = _workspace(ws, x.device)
+    buf = w.get(L.bastion_workspace_bytes(B, K, b, V, k, nmax, dt))
+    mo = MargOut(*[_ptr(out[n]) for n, _ in MargOut._fields_])
+    tst = None if tree is None else _tree_struct(tree)
+    ts = None if tst is None else C.byref(tst)
+    args = (_ptr(x), dt, _ptr(prior_logits), B, K, b, V, x.stride(2), k, nmax, C.byref(mo), ts,
+            _ptr(buf), buf.numel(), _stream())
+    fn = L.bastion_mixture_marginal
+
+    def call(_keep=(mo, tst, buf, x, prior_logits, out, tree)):
+        _check(fn(*args), "bastion_mixture_marginal")
+    return out, tree, call
+
+
+def mixture_marginal(branch_logits, prior_logits, k: int, nmax: int, with_tree: bool = True,
+                     with_mask: bool = True, out=None, tree=None, ws=None):
+    """bastion_mixture_marginal on branch logits [B, K, b, V] and prior logits
+    [B, K] float32: candidates from the mixture marginal and, optionally, the
+    mixture tree over them.  Returns (outputs, tree outputs or None)."""
+    out, tree, call = _marginal_call(branch_logits, prior_logits, k, nmax, with_tree, with_mask,
+                                     out, tree, ws)
+    call()
+    return out, tree
+
+
+def prepare_mixture_marginal(branch_logits, prior_logits, k: int, nmax: int, with_tree: bool = True,
+                             with_mask: bool = True, out=None, tree=None, ws=None):
+    """mixture_marginal with its arguments checked and marshalled once:
+    returns (out, tree, call)."""
+    return _marginal_call(branch_logits, prior_logits, k, nmax, with_tree, with_mask, out, tree, ws)

@@ -307,23 +307,32 @@ int32_t bastion_accept(const int32_t *parent, const int32_t *token, const int32_
                                            accept_nodes, bonus, static_cast<hipStream_t>(stream)));
 }
 
-int32_t bastion_mixture_score(const void *branch_logits, int32_t dtype, const float *prior_logits,
-                              int32_t B, int32_t K, int32_t b, int32_t V, int64_t row_stride,
-                              int32_t k, int32_t nmax, const bastion_mixture_out *mix,
-                              const bastion_tree_out *tree, void *ws, size_t ws_bytes,
-                              void *stream) {
+}  // extern "C"
+
+namespace {
+
+// bastion_mixture_score (mix) or bastion_mixture_marginal (marg), on the
+// caller's workspace
+int32_t mixture_call(const void *branch_logits, int32_t dtype, const float *prior_logits, int32_t B,
+                     int32_t K, int32_t b, int32_t V, int64_t row_stride, int32_t k, int32_t nmax,
+                     const bastion_mixture_out *mix, const bastion_marginal_out *marg,
+                     const bastion_tree_out *tree, void *ws, size_t ws_bytes, void *stream) {
     if (!branch_logits || !prior_logits || (dtype != BASTION_F32 && dtype != BASTION_BF16))
         return BASTION_EINVAL;
     if (K < 1 || K > kMaxBranches || !sizes_ok(B, b, V, k, nmax)) return BASTION_EINVAL;
     if (row_stride < V || (reinterpret_cast<uintptr_t>(branch_logits) % esize(dtype)) != 0)
         return BASTION_EINVAL;
-    if (!mix || !mix->prior_q || !mix->chain_tokens || !mix->qdep_chain || !mix->cand_count ||
-        !mix->cand_tokens || !mix->cand_q || !mix->row_max || !mix->row_sum)
+    if (mix && (!mix->prior_q || !mix->chain_tokens || !mix->qdep_chain || !mix->cand_count ||
+                !mix->cand_tokens || !mix->cand_q || !mix->row_max || !mix->row_sum))
         return BASTION_EINVAL;
+    if (marg && (!marg->prior_q || !marg->row_max || !marg->row_sum || !marg->marg_ids ||
+                 !marg->marg_q || !marg->cand_q))
+        return BASTION_EINVAL;
+    if (!mix == !marg) return BASTION_EINVAL;
     if (tree && !tree_out_ok(tree, false)) return BASTION_EINVAL;
     // the query stage keeps every position's candidates and q tables and the
     // running list in the LDS of one CU
-    if (mix_layout(K, b, k, nmax).total > kMixMaxLds) return BASTION_EUNSUPPORTED;
+    if (mix_layout(K, b, k, nmax, marg ? k : 0).total > kMixMaxLds) return BASTION_EUNSUPPORTED;
     const int64_t rows = int64_t(B) * K * b;
     const int S = plan_segments(rows, V, dtype);
     const Layout L = layout(rows, k, S);
@@ -338,8 +347,8 @@ int32_t bastion_mixture_score(const void *branch_logits, int32_t dtype, const fl
     P.cost = nullptr; P.cost_qstride = 0; P.l_ar = 1.0; P.pos_base = nullptr;
     P.topk_ids = reinterpret_cast<int32_t *>(w + L.mtopk_ids);
     P.topk_q = reinterpret_cast<float *>(w + L.mtopk_q);
-    P.row_max = mix->row_max;
-    P.row_sum = mix->row_sum;
+    P.row_max = mix ? mix->row_max : marg->row_max;
+    P.row_sum = mix ? mix->row_sum : marg->row_sum;
     if (tree) {
         P.parent = tree->parent; P.depth = tree->depth; P.token = tree->token;
         P.rho = tree->rho; P.ahat = tree->ahat; P.n_nodes = tree->n_nodes;
@@ -358,14 +367,46 @@ int32_t bastion_mixture_score(const void *branch_logits, int32_t dtype, const fl
     P.resident_blocks = kBlocksPerCu * device_cus();
     set_stamps(P, rows * S);
     P.prior = prior_logits;
-    P.prior_q = mix->prior_q;
-    P.chain_tokens = mix->chain_tokens;
-    P.qdep = mix->qdep_chain;
-    P.cand_count = mix->cand_count;
-    P.cand_tokens = mix->cand_tokens;
-    P.cand_q = mix->cand_q;
+    P.prior_q = mix ? mix->prior_q : marg->prior_q;
+    if (mix) {
+        P.chain_tokens = mix->chain_tokens;
+        P.qdep = mix->qdep_chain;
+        P.cand_count = mix->cand_count;
+        P.cand_tokens = mix->cand_tokens;
+        P.cand_q = mix->cand_q;
+    } else {
+        P.mix_marginal = 1;
+        P.marg_ids = marg->marg_ids;
+        P.marg_q = marg->marg_q;
+        P.marg_cq = marg->cand_q;
+    }
     P.mix_tree = tree ? 1 : 0;
     return to_status(bastion_launch_build(P, dtype, static_cast<hipStream_t>(stream), nullptr));
+}
+
+
+}  // namespace
+
+extern "C" {
+
+int32_t bastion_mixture_score(const void *branch_logits, int32_t dtype, const float *prior_logits,
+                              int32_t B, int32_t K, int32_t b, int32_t V, int64_t row_stride,
+                              int32_t k, int32_t nmax, const bastion_mixture_out *mix,
+                              const bastion_tree_out *tree, void *ws, size_t ws_bytes,
+                              void *stream) {
+    if (!mix) return BASTION_EINVAL;
+    return mixture_call(branch_logits, dtype, prior_logits, B, K, b, V, row_stride, k, nmax, mix,
+                        nullptr, tree, ws, ws_bytes, stream);
+}
+
+int32_t bastion_mixture_marginal(const void *branch_logits, int32_t dtype,
+                                 const float *prior_logits, int32_t B, int32_t K, int32_t b,
+                                 int32_t V, int64_t row_stride, int32_t k, int32_t nmax,
+                                 const bastion_marginal_out *marg, const bastion_tree_out *tree,
+                                 void *ws, size_t ws_bytes, void *stream) {
+    if (!marg) return BASTION_EINVAL;
+    return mixture_call(branch_logits, dtype, prior_logits, B, K, b, V, row_stride, k, nmax,
+                        nullptr, marg, tree, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -39,6 +39,10 @@ struct BuildParams {
     int32_t *cand_count, *cand_tokens;
     float *cand_q;
     int mix_tree;         // 1: build the mixture tree into parent/depth/...
+    int mix_marginal;     // 1: candidates from the mixture marginal (marg_*)
+    int32_t *marg_ids;    // [B, b, k] tokens ranked by the mixture marginal
+    float *marg_q;        // [B, b, k] their marginal sum_z w_z q_i(x|z)
+    float *marg_cq;       // [B, b, k, K] q_i(x|z) of every branch
     int split_trees;      // 1: the trees run in a launch of their own (mode 0)
     int resident_blocks;  // stream blocks the machine holds at once
     uint64_t *stamps;     // stamped build only: per-block timestamps of the

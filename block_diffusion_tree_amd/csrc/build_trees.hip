@@ -829,8 +829,9 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem, uint64_t *st
 template <int NT>
 __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int K = P.K, b = P.b, k = P.k, C = K * k, nmax = P.nmax;
-    MixLds M = mix_lds(smem, mix_layout(K, b, k, nmax), C);
+    const int K = P.K, b = P.b, k = P.k, nmax = P.nmax;
+    const int C = P.mix_marginal ? k : K * k;
+    MixLds M = mix_lds(smem, mix_layout(K, b, k, nmax, C), C);
     const int64_t r0 = int64_t(q) * K * b;
     __shared__ int s_bad, s_ns, s_np;
     __shared__ uint64_t s_tau;
@@ -845,7 +846,7 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         const int32_t rst = ld_agent(P.row_status + r0 + e);
         if (rst != BASTION_Q_OK) atomicOr(&s_bad, rst == BASTION_Q_RANGE ? 2 : 1);
     }
-    for (int e = tid; e < b * C; e += NT) {
+    for (int e = tid; e < b * C && !P.mix_marginal; e += NT) {
         const int pos = e / C, c = e - pos * C;
         const int z = c / k, j = c - z * k;
         M.ids[e] = ld_agent(P.topk_ids + (r0 + z * b + pos) * k + j);
@@ -869,6 +870,12 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
     }
     __syncthreads();
     const int64_t cbase = int64_t(q) * b * C;
+    if (s_bad && P.mix_marginal) {
+        // the marginal pass wrote the (empty) candidates; the root alone
+        emit_tree<NT>(P, q, M.par, M.dep, M.tok, M.rho, M.ahat, 0, true,
+                      (s_bad & 1) ? BASTION_Q_BAD_LOGITS : BASTION_Q_RANGE);
+        return;
+    }
     if (s_bad) {
         // a bad branch row: no chains, no candidates, the root alone
         for (int e = tid; e < K * b; e += NT) P.chain_tokens[r0 + e] = -1;
@@ -881,6 +888,18 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
                           (s_bad & 1) ? BASTION_Q_BAD_LOGITS : BASTION_Q_RANGE);
         return;
     }
+    if (P.mix_marginal) {
+        // candidates of the marginal pass: k per position, with every
+        // branch's q, into the tables the rounds read
+        for (int e = tid; e < b * C; e += NT) {
+            const int pos = e / C, c = e - pos * C;
+            const int64_t o = (int64_t(q) * b + pos) * C + c;
+            M.ctok[e] = P.marg_ids[o];
+            for (int z = 0; z < K; ++z) M.cq[(pos * K + z) * C + c] = P.marg_cq[o * K + z];
+        }
+        for (int i = tid; i < b; i += NT) M.cnt[i] = C;
+        __syncthreads();
+    } else {
     // chains: the top-1 token of every branch row (chain[z * b + i])
     for (int e = tid; e < K * b; e += NT) {
         const int z = e / b, i = e - z * b;
@@ -998,6 +1017,7 @@ __device__ void mixture_stage(const BuildParams &P, int q, char *smem) {
         for (int zp = 0; zp < K; ++zp) qd += M.w[zp] * M.prod[z * K + zp];
         P.qdep[q * K + z] = qd;
     }
+    }   // unions, gathers and q_dep of the branch chains
     if (!P.mix_tree) return;
     // the tree, round by round (each position's q table is in LDS).  The
     // running list and the parent table are double-buffered: a merge writes
@@ -1260,6 +1280,150 @@ __global__ __launch_bounds__(kThreads, (R >= 16 ? 2 : 4)) void build_trees_kerne
     tree_stage<R>(P, q, smem, P.stamps);
 }
 
+// ---------------------------------------------------------------------------
+// Candidates from the latent mixture's marginal (DBlast page, Methodology 1:
+// q_dep mixes the branches with weights q(z|y), so position i's marginal is
+// m_i(x) = sum_z q(z|y) q_i(x|y,z)): one block per (query, position), after
+// the stream launch left every branch row's max and sum.  The block streams
+// the K branch rows of its position together, forms
+// m(x) = sum_z (w_z / S_z) 2^(l_z(x) log2 e - c_z) in float32 (w_z / S_z
+// rounded once from float64) and keeps the k largest (m desc, token asc)
+// with the stream's threshold-filtered candidate buffers.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void marginal_kernel(BuildParams P) {
+    extern __shared__ __align__(16) char smem[];
+    constexpr int U = 4;
+    constexpr int E = Elem<T>::kPerVec;
+    const int b = P.b, K = P.K, k = P.k, V = P.V;
+    const int q = blockIdx.x / b, i = blockIdx.x - q * b;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t r0 = int64_t(q) * K * b;   // the query's first branch row
+    const int64_t ob = (int64_t(q) * b + i) * k;
+    __shared__ float s_a[kMaxBranches], s_c[kMaxBranches], s_s[kMaxBranches];
+    __shared__ int s_bad;
+    __shared__ uint64_t s_bth;
+    if (tid == 0) {
+        s_bad = 0;
+        s_bth = 0;
+    }
+    __syncthreads();
+    for (int e = tid; e < K * b; e += kThreads)
+        if (ld_agent(P.row_status + r0 + e) != BASTION_Q_OK) atomicOr(&s_bad, 1);
+    if (wv == 0) {
+        // prior weights in float64, as the mixture stage forms them
+        const double pz = lane < K ? double(P.prior[q * K + lane]) : -INFINITY;
+        double pm = pz;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) pm = fmax(pm, __shfl_xor(pm, o));
+        const double ez = lane < K ? exp(pz - pm) : 0.0;
+        double ps = 0.0;
+        for (int z = 0; z < K; ++z) ps += __shfl(ez, z);
+        if (lane < K) {
+            const int64_t row = r0 + int64_t(lane) * b + i;
+            const float M = ld_agent(P.row_ms + 2 * row), S = ld_agent(P.row_ms + 2 * row + 1);
+            s_c[lane] = scale_ref(M);
+            s_s[lane] = S;
+            s_a[lane] = float((ez / ps) / double(S));
+            if (i == 0) P.prior_q[q * K + lane] = float(ez / ps);
+        }
+    }
+    __syncthreads();
+    if (s_bad) {
+        for (int j = tid; j < k; j += kThreads) {
+            P.marg_ids[ob + j] = -1;
+            P.marg_q[ob + j] = 0.0f;
+            for (int z = 0; z < K; ++z) P.marg_cq[(ob + j) * K + z] = 0.0f;
+        }
+        return;
+    }
+    WaveScratch<U> *scr = reinterpret_cast<WaveScratch<U> *>(smem);
+    Streamer<T, U> st;
+    st.ws = &scr[wv];
+    st.k = k;
+    st.thv = -INFINITY;
+    st.thk = 0;
+    st.cnt = 0;
+    st.nstage = 0;
+    st.head = 0;
+    st.booted = true;
+    st.bth = &s_bth;
+    const char *base = P.logits + (r0 + i) * P.row_stride_bytes;   // branch z: + z * b rows
+    const int64_t zstride = int64_t(b) * P.row_stride_bytes;
+    // 16-byte vectors when every row of the position starts on 16 bytes
+    const bool vec = ((reinterpret_cast<uintptr_t>(base) | uintptr_t(zstride)) & 15u) == 0;
+    const int nvec = vec ? V / E : 0;
+    for (int v0 = 0; v0 < nvec; v0 += kThreads) {
+        const int v = v0 + tid;
+        const bool ok = v < nvec;
+        float m[E];
+#pragma unroll
+        for (int j = 0; j < E; ++j) m[j] = 0.0f;
+#pragma unroll 4
+        for (int z = 0; z < K; ++z) {
+            const u32x4 raw = load_vec<T>(base + z * zstride, ok ? v : nvec - 1);
+            float f[E];
+            Elem<T>::decode(raw, f);
+            const float a = s_a[z], c = s_c[z];
+#pragma unroll
+            for (int j = 0; j < E; ++j)
+                m[j] += a * __builtin_amdgcn_exp2f(__builtin_fmaf(f[j], kLog2e, -c));
+        }
+        float vmax = m[0];
+#pragma unroll
+        for (int j = 1; j < E; ++j) vmax = fmaxf(vmax, m[j]);
+        const uint64_t bk = s_bth;
+        if (bk > st.thk) {
+            st.thk = bk;
+            st.thv = topk_key_value(bk);
+        }
+        if (__ballot(ok && vmax >= st.thv)) {
+#pragma unroll
+            for (int j = 0; j < E; ++j)
+                st.offer_scalar(ok && m[j] >= st.thv, m[j], uint32_t(v * E + j));
+        }
+    }
+    // elements after the last vector (or every element of unaligned rows)
+    for (int e0 = nvec * E; e0 < V; e0 += kThreads) {
+        const int e = e0 + tid;
+        const bool ok = e < V;
+        float m = 0.0f;
+        for (int z = 0; z < K && ok; ++z)
+            m += s_a[z] * __builtin_amdgcn_exp2f(
+                              __builtin_fmaf(Elem<T>::at(base + z * zstride, e), kLog2e, -s_c[z]));
+        st.offer_scalar(ok, m, uint32_t(e));
+    }
+    if (st.cnt > kWave) st.compact();
+    // block merge: wave 0 gathers every wave's keys and selects the k best
+    __shared__ int red_n[kWavesPerBlock];
+    if (lane == 0) red_n[wv] = st.cnt;
+    __syncthreads();
+    if (wv == 0) {
+        int total = red_n[0];
+        for (int w = 1; w < kWavesPerBlock; ++w) {
+            const int nw = red_n[w];
+            if (lane < nw) scr[0].cand[total + lane] = scr[w].cand[lane];
+            total += nw;
+        }
+        wave_sync();
+        uint64_t kth;
+        const int nsel = wave_select_topk<kCap / kWave>(scr[0].cand, total, k, kth);
+        if (lane < k) {
+            const uint64_t key = lane < nsel ? scr[0].cand[lane] : 0;
+            const int tok = lane < nsel ? topk_key_token(key) : -1;
+            P.marg_ids[ob + lane] = tok;
+            P.marg_q[ob + lane] = lane < nsel ? topk_key_value(key) : 0.0f;
+            for (int z = 0; z < K; ++z) {
+                // the branch row's own q formula at the token
+                const float l = tok >= 0 ? Elem<T>::at(base + z * zstride, tok) : 0.0f;
+                P.marg_cq[(ob + lane) * K + z] =
+                    tok >= 0 ? __builtin_amdgcn_exp2f(__builtin_fmaf(l, kLog2e, -s_c[z])) / s_s[z]
+                             : 0.0f;
+            }
+        }
+    }
+}
+
 // The latent-mixture stage, one block per query, launched after the stream
 // kernel on the same stream.  A mixture stage is long (every position's
 // unions, gathers and a tree round per position); run inside the stream
@@ -1319,7 +1483,12 @@ static hipError_t launch_r(const BuildParams &P, int smem, hipStream_t s) {
     if (P.mode == 1) {
         const hipError_t e = launch_one<T, U, 1, 1>(P, smem, s);
         if (e != hipSuccess) return e;
-        const int msmem = mix_layout(P.K, P.b, P.k, P.nmax).total;
+        if (P.mix_marginal) {
+            hipLaunchKernelGGL(marginal_kernel<T>, dim3(unsigned(P.B * P.b)), dim3(kThreads),
+                               int(sizeof(WaveScratch<U>)) * kWavesPerBlock, s, P);
+            if (!P.mix_tree) return hipGetLastError();
+        }
+        const int msmem = mix_layout(P.K, P.b, P.k, P.nmax, P.mix_marginal ? P.k : 0).total;
         if (msmem > 65536) {
             const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void *>(mixture_kernel),
                                                       hipFuncAttributeMaxDynamicSharedMemorySize, msmem);

@@ -46,9 +46,12 @@ __host__ __device__ inline int mix_align16(int x) { return (x + 15) & ~15; }
 // flags, the chains' q); arrays used only by the rounds.  The last two share
 // space.  The stage has a launch of its own, one block per CU, so the
 // layout may use up to kMixMaxLds bytes.
-__host__ __device__ inline MixLayout mix_layout(int K, int b, int k, int nmax) {
+// C: candidate slots per position (K * k for the unions of the branches'
+// top-k, k for the marginal's top-k)
+__host__ __device__ inline MixLayout mix_layout(int K, int b, int k, int nmax, int C = 0) {
     MixLayout L;
-    const int C = K * k, nn = nmax + 2;
+    C = C > 0 ? C : K * k;
+    const int nn = nmax + 2;
     int o = 0;
     L.w = o;     o = mix_align16(o + 8 * K);
     L.wq = o;    o = mix_align16(o + 4 * K);

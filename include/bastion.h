@@ -284,6 +284,37 @@ int32_t bastion_mixture_score(const void *branch_logits, int32_t dtype,
                               const bastion_mixture_out *mix, const bastion_tree_out *tree,
                               void *ws, size_t ws_bytes, void *stream);
 
+/* Outputs of the mixture-marginal call. */
+typedef struct bastion_marginal_out {
+    float *prior_q;        /* [B, K]        q(z|y) = softmax of the prior logits  */
+    float *row_max;        /* [B, K, b]     per-branch row statistics             */
+    float *row_sum;        /* [B, K, b]                                           */
+    int32_t *marg_ids;     /* [B, b, k]     tokens ranked by the marginal         */
+    float *marg_q;         /* [B, b, k]     their marginal sum_z q(z|y) q_i(x|z)  */
+    float *cand_q;         /* [B, b, k, K]  q_i(token | z) of every branch        */
+} bastion_marginal_out;
+
+/*
+ * bastion_mixture_marginal -- [DBLAST] Methodology 1: the latent mixture
+ * mixes its branches with weights q(z|y), so position i's marginal is
+ * m_i(x) = sum_z q(z|y) q_i(x|y,z).  Candidates of position i: the k tokens
+ * ranked first by (m_i desc, token asc), with m_i and every branch's
+ * q_i(x|z) (an alternative to bastion_mixture_score's union of the branches'
+ * top-k).  m is formed in float32 as sum_z (q(z|y) / S_z) 2^(l log2 e - c_z)
+ * from each branch row's max and sum (a first streaming pass), so two
+ * tokens whose marginals agree to float32 rounding may rank either way.
+ * Tree (when tree != NULL): best-first over these candidates with the
+ * mixture score of bastion_mixture_score.  Three launches: the branch rows'
+ * statistics, the marginal pass (one block per query and position, reading
+ * the K rows of its position once more), the tree stage.
+ * Arguments, workspace and errors as bastion_mixture_score.
+ */
+int32_t bastion_mixture_marginal(const void *branch_logits, int32_t dtype,
+                                 const float *prior_logits, int32_t B, int32_t K, int32_t b,
+                                 int32_t V, int64_t row_stride, int32_t k, int32_t nmax,
+                                 const bastion_marginal_out *marg, const bastion_tree_out *tree,
+                                 void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
