@@ -757,3 +757,121 @@ void oracle_mixture_tree(const float *w, const int32_t *cand_count,
         free(rnode);
     }
 }
+
+/* ------------------------------------------------------------------------
+ * Stochastic variants.
+ *
+ * Counter-based uniforms: the MurmurHash3 32-bit finalizer (fmix32, Austin
+ * Appleby, public domain) applied to a key built from (seed, query, node,
+ * token); u = ((h >> 8) + 1/2) / 2^24, in (0, 1).  The key:
+ *   a = fmix32(seed + 0x9E3779B9 (q + 1)),
+ *   c = fmix32(a ^ 0x85EBCA6B (node + 1)),
+ *   h = fmix32(c ^ token),   all arithmetic mod 2^32.
+ * ------------------------------------------------------------------------ */
+static uint32_t fmix32(uint32_t h)
+{
+    h ^= h >> 16;
+    h *= 0x85EBCA6Bu;
+    h ^= h >> 13;
+    h *= 0xC2B2AE35u;
+    h ^= h >> 16;
+    return h;
+}
+
+static double uniform_at(uint32_t seed, uint32_t q, uint32_t node, uint32_t token)
+{
+    uint32_t a = fmix32(seed + 0x9E3779B9u * (q + 1u));
+    uint32_t c = fmix32(a ^ (0x85EBCA6Bu * (node + 1u)));
+    uint32_t h = fmix32(c ^ token);
+    return ((double)(h >> 8) + 0.5) / 16777216.0;
+}
+
+/*
+ * A draw from the target's distribution at every tree node  [B-Res] with a
+ * target temperature (the DBlast page evaluates targets at temperatures
+ * 0.7-1.5, Problem statement and Experimental results): node i of query q
+ * draws x from softmax(l / T) of its logits row, by the Gumbel-max rule
+ * x = argmax_v (l_v / T + g_v), g_v = -log(-log(u_v)) (ties: smaller token);
+ * T = 0 is the argmax of l (greedy).  float64.  Rows after n_nodes[q] get
+ * -1.  logits [B, nmax+1, V] (row_stride between nodes); sampled and score
+ * [B, nmax+1] (score: the winning l/T + g, or l for T = 0).
+ */
+void oracle_sample_nodes(const void *logits, int dtype, int B, int nmax, int V,
+                         int64_t row_stride, const int32_t *n_nodes, double temperature,
+                         uint32_t seed, int32_t *sampled, double *score)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < (int64_t)B * (nmax + 1); ++r) {
+        int q = (int)(r / (nmax + 1)), node = (int)(r - (int64_t)q * (nmax + 1));
+        if (node > n_nodes[q]) {
+            sampled[r] = -1;
+            score[r] = 0.0;
+            continue;
+        }
+        int best = -1;
+        double bs = -INFINITY;
+        for (int v = 0; v < V; ++v) {
+            double l = logit_at(logits, dtype, r * row_stride + v);
+            double sc = l;
+            if (temperature > 0.0) {
+                double u = uniform_at(seed, (uint32_t)q, (uint32_t)node, (uint32_t)v);
+                sc = l / temperature - log(-log(u));
+            }
+            if (best < 0 || sc > bs) {
+                best = v;
+                bs = sc;
+            }
+        }
+        sampled[r] = best;
+        score[r] = bs;
+    }
+}
+
+/*
+ * The uniform of (seed, q, node, token) as defined above (exposed so that
+ * tests can check draws against it).
+ */
+double oracle_uniform_at(uint32_t seed, uint32_t q, uint32_t node, uint32_t token)
+{
+    return uniform_at(seed, q, node, token);
+}
+
+/*
+ * DBlast branch sampling  [D-M1] (at inference one branch is decoded
+ * greedily; the latent category is drawn with a temperature Z_T):
+ * z = the smallest index with u < sum_{z' <= z} w_z', w = softmax(prior / Z_T)
+ * in float64 (Z_T = 0: the argmax of the prior, ties to the smaller index).
+ * draft[q] = chain_tokens[q, z].  u [B] in [0, 1).
+ */
+void oracle_mixture_sample(const float *prior_logits, int B, int K, double temperature,
+                           const double *u, const int32_t *chain_tokens, int b,
+                           int32_t *z_out, int32_t *draft)
+{
+    for (int q = 0; q < B; ++q) {
+        int z = 0;
+        if (temperature <= 0.0) {
+            for (int j = 1; j < K; ++j)
+                if (prior_logits[q * K + j] > prior_logits[q * K + z])
+                    z = j;
+        } else {
+            double pm = -INFINITY, ps = 0.0;
+            for (int j = 0; j < K; ++j)
+                if ((double)prior_logits[q * K + j] / temperature > pm)
+                    pm = (double)prior_logits[q * K + j] / temperature;
+            for (int j = 0; j < K; ++j)
+                ps += exp((double)prior_logits[q * K + j] / temperature - pm);
+            double cdf = 0.0;
+            z = K - 1;
+            for (int j = 0; j < K; ++j) {
+                cdf += exp((double)prior_logits[q * K + j] / temperature - pm) / ps;
+                if (u[q] < cdf) {
+                    z = j;
+                    break;
+                }
+            }
+        }
+        z_out[q] = z;
+        for (int i = 0; i < b; ++i)
+            draft[(int64_t)q * b + i] = chain_tokens[((int64_t)q * K + z) * b + i];
+    }
+}

@@ -65,11 +65,16 @@ def _declare(L):
                                  P, P, P, P, P, P, P]
     L.oracle_qdep_sequences.argtypes = [P, I32, P, I32, I32, I32, I32, I64, P, I32, P]
     L.oracle_mixture_marginal.argtypes = [P, I32, P, I32, I32, I32, I32, I64, I32, P, P, P, P, P]
+    L.oracle_sample_nodes.argtypes = [P, I32, I32, I32, I32, I64, P, F64, C.c_uint32, P, P]
+    L.oracle_uniform_at.argtypes = [C.c_uint32] * 4
+    L.oracle_uniform_at.restype = F64
+    L.oracle_mixture_sample.argtypes = [P, I32, I32, F64, P, P, I32, P, P]
     L.oracle_mixture_tree.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32,
                                       P, P, P, P, P, P, P]
     for f in ("oracle_softmax_topk", "oracle_best_first", "oracle_budget_select",
               "oracle_tree_mask", "oracle_accept", "oracle_mixture",
-              "oracle_qdep_sequences", "oracle_mixture_tree", "oracle_mixture_marginal"):
+              "oracle_qdep_sequences", "oracle_mixture_tree", "oracle_mixture_marginal",
+              "oracle_sample_nodes", "oracle_mixture_sample"):
         getattr(L, f).restype = None
 
 
@@ -214,6 +219,39 @@ def mixture_marginal(branch_logits, prior_logits, k: int):
                                   _p(out["marg_ids"]), _p(out["marg_p"]), _p(out["cand_p"]),
                                   _p(out["row_status"]))
     return out
+
+
+def sample_nodes(logits, n_nodes, temperature: float, seed: int):
+    """One draw per tree node from softmax(logits / T) (Gumbel-max with the
+    counter-based uniforms): logits [B, nmax+1, V] (float32 or bf16 bits) ->
+    (sampled [B, nmax+1] int32, score [B, nmax+1] float64)."""
+    a, dt = _raw_logits(logits)
+    B, W1, V = a.shape
+    nn = _c(n_nodes, np.int32)
+    sampled = np.empty((B, W1), np.int32)
+    score = np.empty((B, W1), np.float64)
+    lib().oracle_sample_nodes(_p(a), dt, B, W1 - 1, V, V, _p(nn), float(temperature),
+                              int(seed) & 0xFFFFFFFF, _p(sampled), _p(score))
+    return sampled, score
+
+
+def uniform_at(seed: int, q: int, node: int, token: int) -> float:
+    return float(lib().oracle_uniform_at(seed & 0xFFFFFFFF, q, node, token))
+
+
+def mixture_sample(prior_logits, temperature: float, u, chain_tokens):
+    """Branch draw z ~ softmax(prior / T) by inverse CDF at u [B], and the
+    drafted chain of that branch: (z [B], draft [B, b])."""
+    pr = _c(prior_logits, np.float32)
+    B, K = pr.shape
+    ch = _c(chain_tokens, np.int32)
+    b = ch.shape[2]
+    uu = _c(u, np.float64)
+    z = np.empty(B, np.int32)
+    draft = np.empty((B, b), np.int32)
+    lib().oracle_mixture_sample(_p(pr), B, K, float(temperature), _p(uu), _p(ch), b, _p(z),
+                                _p(draft))
+    return z, draft
 
 
 def qdep_sequences(branch_logits, prior_logits, seqs):
