@@ -84,6 +84,11 @@ def lib():
         L.bastion_mixture_marginal.restype = I32
         L.bastion_mixture_marginal.argtypes = [P, I32, P, I32, I32, I32, I32, I64, I32, I32,
                                                C.POINTER(MargOut), C.POINTER(TreeOut), P, SZ, P]
+        L.bastion_sample_nodes.restype = I32
+        L.bastion_sample_nodes.argtypes = [P, I32, I32, I32, I32, I64, P, C.c_float, C.c_uint32,
+                                           P, P]
+        L.bastion_mixture_sample.restype = I32
+        L.bastion_mixture_sample.argtypes = [P, I32, I32, F64, P, P, I32, P, P, P]
         L.bastion_set_tuning.restype = None
         L.bastion_set_tuning.argtypes = [I32, I32]
         L.bastion_mixture_score.restype = I32
@@ -591,3 +596,43 @@ def prepare_mixture_marginal(branch_logits, prior_logits, k: int, nmax: int, wit
     """mixture_marginal with its arguments checked and marshalled once:
     returns (out, tree, call)."""
     return _marginal_call(branch_logits, prior_logits, k, nmax, with_tree, with_mask, out, tree, ws)
+
+
+def sample_nodes(logits, n_nodes, temperature: float, seed: int, out=None):
+    """bastion_sample_nodes: logits [B, nmax+1, V] (float32 or bfloat16, the
+    target's logits at every tree node), n_nodes [B] int32 -> one draw per
+    node, int32 [B, nmax+1] (-1 after n_nodes)."""
+    _dev(logits, "logits")
+    if logits.dim() != 3 or logits.stride(2) != 1 or logits.stride(0) != logits.size(1) * logits.stride(1):
+        raise ValueError("logits must be [B, nmax+1, V] with unit stride over V and rows packed")
+    B, W1, V = logits.shape
+    _need(n_nodes, "n_nodes", torch.int32, (B,), logits.device)
+    if out is None:
+        out = torch.empty((B, W1), dtype=torch.int32, device=logits.device)
+    _need(out, "sampled", torch.int32, (B, W1), logits.device)
+    _check(lib().bastion_sample_nodes(_ptr(logits), _dtype_code(logits), B, W1 - 1, V,
+                                      logits.stride(1), _ptr(n_nodes), float(temperature),
+                                      int(seed) & 0xFFFFFFFF, _ptr(out), _stream()),
+           "bastion_sample_nodes")
+    return out
+
+
+def mixture_sample(prior_logits, temperature: float, u, chain_tokens):
+    """bastion_mixture_sample: prior [B, K] float32, u [B] float64, chains
+    [B, K, b] int32 -> (z [B], draft [B, b])."""
+    if prior_logits.dim() != 2:
+        raise ValueError("prior_logits must be [B, K]")
+    B, K = prior_logits.shape
+    dev = prior_logits.device
+    _need(prior_logits, "prior_logits", torch.float32, (B, K), dev)
+    _need(u, "u", torch.float64, (B,), dev)
+    if chain_tokens.dim() != 3:
+        raise ValueError("chain_tokens must be [B, K, b]")
+    b = chain_tokens.size(2)
+    _need(chain_tokens, "chain_tokens", torch.int32, (B, K, b), dev)
+    z = torch.empty((B,), dtype=torch.int32, device=dev)
+    draft = torch.empty((B, b), dtype=torch.int32, device=dev)
+    _check(lib().bastion_mixture_sample(_ptr(prior_logits), B, K, float(temperature), _ptr(u),
+                                        _ptr(chain_tokens), b, _ptr(z), _ptr(draft), _stream()),
+           "bastion_mixture_sample")
+    return z, draft

@@ -21,7 +21,8 @@ LIB = os.path.join(PKG, "libbastion.so")
 # the streaming-read ceiling the benchmark measures beside the kernels
 PROBE_LIB = os.path.join(PKG, "libbastion_probe.so")
 PROBE_SOURCES = ["stream_probe.hip"]
-SOURCES = ["api.hip", "build_trees.hip", "tree_ops.hip", "noalloc.hip", "verify.hip"]
+SOURCES = ["api.hip", "build_trees.hip", "tree_ops.hip", "noalloc.hip", "verify.hip",
+           "stochastic.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

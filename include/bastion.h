@@ -315,6 +315,47 @@ int32_t bastion_mixture_marginal(const void *branch_logits, int32_t dtype,
                                  const bastion_marginal_out *marg, const bastion_tree_out *tree,
                                  void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * bastion_sample_nodes -- sampled (non-greedy) verification: one draw per
+ * tree node from the target's distribution at temperature T.  [BASTION]
+ * Experimental results evaluate greedy decoding; [DBLAST] Problem statement
+ * and Experimental results evaluate targets at temperatures 0.7-1.5.  The
+ * pages give no acceptance rule for sampled tree verification; this is the
+ * target-sampling walk (SpecInfer's naive sampling, Miao et al. 2024):
+ * bastion_accept with these draws as `target` moves from the root to the
+ * child whose token equals the current node's draw until none does, and
+ * commits that draw as the bonus -- lossless for any fixed tree.
+ * logits [B, nmax+1, V] (row (q, i) at element (q*(nmax+1) + i)*row_stride):
+ *   the target's logits after node i's path, finite or -inf.
+ * sampled [B, nmax+1]: for i <= n_nodes[q] the draw
+ *   x = argmax_v (l_v / T + g_v) (ties: smaller token), g_v = -log(-log(u_v)),
+ *   computed in float32; T = 0 draws the argmax of l.  Entries after
+ *   n_nodes[q] are -1.  The uniforms are counter-based (MurmurHash3's 32-bit
+ *   finalizer fmix32): with a = fmix32(seed + 0x9E3779B9 (q+1)),
+ *   c = fmix32(a ^ 0x85EBCA6B (i+1)), h = fmix32(c ^ v) (mod 2^32),
+ *   u_v = ((h >> 8) + 1/2) / 2^24; the same seed gives the same draws.
+ * Errors: EINVAL for null pointers, sizes outside the limits (0 <= nmax <=
+ *   1023, V <= 524288), row_stride < V, a misaligned pointer, T < 0 or not
+ *   finite.
+ */
+int32_t bastion_sample_nodes(const void *logits, int32_t dtype, int32_t B, int32_t nmax, int32_t V,
+                             int64_t row_stride, const int32_t *n_nodes, float temperature,
+                             uint32_t seed, int32_t *sampled, void *stream);
+
+/*
+ * bastion_mixture_sample -- [DBLAST] Methodology 1, inference: the latent
+ * category is drawn with a temperature Z_T and its branch decoded greedily.
+ * z[q] = the smallest index with u[q] < sum_{z' <= z} w_z',
+ * w = softmax(prior_logits[q] / Z_T) in float64 (Z_T = 0: the argmax, ties
+ * to the smaller index); draft[q, :] = chain_tokens[q, z, :] (the greedy
+ * chains of bastion_mixture_score).  u [B] float64 in [0, 1), supplied by
+ * the caller.  Errors: EINVAL for null pointers, K or b outside the limits,
+ * Z_T < 0 or not finite.
+ */
+int32_t bastion_mixture_sample(const float *prior_logits, int32_t B, int32_t K, double temperature,
+                               const double *u, const int32_t *chain_tokens, int32_t b,
+                               int32_t *z_out, int32_t *draft, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
