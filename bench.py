@@ -32,6 +32,9 @@ WORKLOAD_TEXT = {
     "latency": "B=1 x b=16 x V=151936 bf16 logits, k=16, online stop over N<=128",
     "tiny": "B=1 x b=4 x V=1024 fp32 logits, k=4, fixed N=32",
     "mixture": "B=128 queries x K=8 branches x b=16 x V=151936 bf16 logits, k=8, mixture tree N=64",
+    "verify": "one attention layer of the verify pass over the main workload's 64 trees (N=64, "
+              "T=65 tree tokens each): 32 query / 8 KV heads of 128, bf16 KV cache, contexts "
+              "U[512, 8192]",
 }
 HBM_PEAK_GBS = 8000.0
 N_BUFFERS = 4
@@ -238,6 +241,125 @@ def time_launches(fn, n, stream):
     return np.array([a.elapsed_time(b) for a, b in ev])
 
 
+def verify_bytes_flops(vw, ctx):
+    """Algorithmic bytes and flops of one tree_attention call: every cached
+    and tree key's k and v read once, the qkv rows read once, the output and
+    the tree tokens' cache slots written once; q.k and p.v over every visible
+    or masked key of a sequence's last chunk alike (4 Hq D T (ctx + T))."""
+    import numpy as np
+    keys = np.minimum(np.maximum(ctx.astype(np.int64), 0), vw.lmax - vw.T) + vw.T
+    kv = 2 * vw.Hkv * vw.D * 2                      # bytes of one key's k and v
+    rows = vw.S * vw.T
+    nbytes = int(kv * keys.sum() + rows * (vw.Hq + 2 * vw.Hkv) * vw.D * 2
+                 + rows * vw.Hq * vw.D * 2 + rows * kv)
+    flops = float(4 * vw.Hq * vw.D * vw.T * keys.sum())
+    return nbytes, flops
+
+
+def cpu_baseline_verify(qkv, kc, vc, ctx, pos, mask, inv, vw, out, budget_s=10.0, max_seq=16):
+    """The CPU reference on a bounded sample (sequences in order of their
+    context length, shortest first, until about budget_s seconds of CPU time
+    or max_seq sequences), with a parity check of the GPU output on them."""
+    import numpy as np
+    import torch
+    from oracle import verify_oracle as vo
+    order = []
+    secs, ok, worst = 0.0, True, 0.0
+    T, D = vw.T, vw.D
+    for s in np.argsort(ctx, kind="stable"):
+        if secs >= budget_s or len(order) >= max_seq:
+            break
+        order.append(int(s))
+        s = int(s)
+        rows = qkv[s * T:(s + 1) * T].double().cpu().numpy()
+        kcs = kc[s:s + 1].double().cpu().numpy()
+        vcs = vc[s:s + 1].permute(0, 1, 3, 2, 4).reshape(1, vw.Hkv, D, vw.lmax).double().cpu().numpy()
+        t0 = time.perf_counter()
+        ref, _, _ = vo.tree_attention(rows, 1, T, vw.Hq, vw.Hkv, D, kcs, vcs, ctx[s:s + 1],
+                                      pos[s:s + 1], mask[s:s + 1], inv)
+        secs += time.perf_counter() - t0
+        got = out[s * T:(s + 1) * T].double().cpu().numpy()
+        vmax = max(np.abs(rows[:, (vw.Hq + vw.Hkv) * D:]).max(), np.abs(vcs).max())
+        err = np.abs(got - ref)
+        bound = 2.0 ** -8 * vmax + 2.0 ** -8 * np.abs(ref)
+        ok = ok and bool((err <= bound).all())
+        worst = max(worst, float((err / bound).max()))
+    threads = torch.get_num_threads()
+    n_seq = len(order)
+    return ({"value": n_seq / secs, "unit": "sequences/s (one attention layer)",
+             "cores": threads, "kind": "oracle",
+             "sample": f"{n_seq} of {vw.S} sequences, the shortest contexts "
+                       f"({int(ctx[order[0]])}..{int(ctx[order[-1]])} cached tokens, mean "
+                       f"{float(np.mean(ctx)):.0f} over all 64), float64 numpy; {secs:.1f} s"},
+            {"sequences": [int(i) for i in order], "within_tolerance": ok,
+             "max_err_over_bound": worst})
+
+
+def main_verify(args):
+    """--workload verify: a step is one bastion_tree_attention call (cache
+    append, attention, split combine) over the 64 trees that
+    bastion_build_trees makes of one main-workload batch."""
+    import numpy as np
+    import torch
+    from block_diffusion_tree_amd import binding, synth
+    vw = synth.VERIFY_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    binding.lib()
+    wl = synth.WORKLOADS["main"]
+    assert wl.B == vw.S and wl.nmax + 1 == vw.T
+    ctx_np = synth.make_verify_contexts(vw)
+    ctx = torch.from_numpy(ctx_np).to(dev)
+    x = synth.make_logits(wl, device=dev)
+    trees = binding.build_trees(x, k=wl.k, nmax=wl.nmax, pos_base=ctx)
+    mask, pos = trees["mask"], trees["position_ids"]
+    del x
+    qkv, kc, vc = synth.make_verify_tensors(vw, device=dev)
+    inv = binding.rope_inv_freq(1.0e6, vw.D, dev)
+    out, call = binding.prepare_tree_attention(qkv, vw.S, vw.T, vw.Hq, vw.Hkv, kc, vc, ctx, pos,
+                                               mask, inv, max_ctx=vw.ctx_hi)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    launch_ms = time_launches(lambda i: call(), args.steps, stream)
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    nbytes, flops = verify_bytes_flops(vw, ctx_np)
+    mean_ms = float(launch_ms.mean())
+    achieved = nbytes / (mean_ms * 1e-3) / 1e9
+    line = {
+        "metric": "tree-attention layer: verified trees/sec + achieved HBM GB/s, S=64 T=65, 1 MI355X",
+        "value": vw.S / (ms_per_step * 1e-3),
+        "unit": "trees/s (one attention layer)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}",
+                   "lmax": vw.lmax, "mean_ctx": float(ctx_np.mean())},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "append_kernel + attention_kernel + combine_kernel: the launches "
+                               "of one bastion_tree_attention call, timed together",
+                     "alg_bytes_per_launch": nbytes,
+                     "launch_us_mean": mean_ms * 1e3,
+                     "launch_us_p50": float(np.median(launch_ms)) * 1e3,
+                     "mfma": {"flops_per_launch": flops,
+                              "achieved_tflops": flops / (mean_ms * 1e-3) / 1e12,
+                              "peak_tflops": 2500.0,
+                              "frac": flops / (mean_ms * 1e-3) / 2.5e15}},
+    }
+    if not args.no_cpu_baseline:
+        base, par = cpu_baseline_verify(qkv, kc, vc, ctx_np, pos.cpu().numpy(),
+                                        mask.cpu().numpy().view(np.uint32),
+                                        inv.cpu().numpy(), vw, out)
+        line["cpu_baseline"] = base
+        line["parity_sample"] = par
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -245,6 +367,9 @@ def main():
               "the path shards over queries with no exchange, so N GPUs run N copies.",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload == "verify":
+        main_verify(args)
+        return
     import numpy as np
     import torch
     from block_diffusion_tree_amd import binding, synth

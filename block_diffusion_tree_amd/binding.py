@@ -412,6 +412,14 @@ def rope_inv_freq(theta: float = 1.0e6, head_dim: int = 128, device="cuda"):
 
 def tree_attention(qkv, S: int, T: int, Hq: int, Hkv: int, k_cache, v_cache, ctx_len,
                    position_ids, mask, inv_freq, out=None, ws=None, max_ctx: int = -1):
+    out, call = prepare_tree_attention(qkv, S, T, Hq, Hkv, k_cache, v_cache, ctx_len,
+                                       position_ids, mask, inv_freq, out, ws, max_ctx)
+    call()
+    return out
+
+
+def prepare_tree_attention(qkv, S: int, T: int, Hq: int, Hkv: int, k_cache, v_cache, ctx_len,
+                           position_ids, mask, inv_freq, out=None, ws=None, max_ctx: int = -1):
     """bastion_tree_attention: qkv [S*T, >= (Hq+2Hkv)*128] bf16 rows (unit
     stride over columns), k_cache [S, Hkv, Lmax, 128] and v_cache
     [S, Hkv, Lmax/32, 128, 32] bf16 (32-slot tiles; the tree tokens are
@@ -453,12 +461,15 @@ def tree_attention(qkv, S: int, T: int, Hq: int, Hkv: int, k_cache, v_cache, ctx
         ws = buf
     if ws.numel() < need:
         raise ValueError(f"workspace needs {need} bytes")
-    _check(L.bastion_tree_attention(_ptr(qkv), qkv.stride(0), S, T, Hq, Hkv, D, _ptr(k_cache),
-                                    _ptr(v_cache), Lmax, _ptr(ctx_len), int(max_ctx),
-                                    _ptr(position_ids),
-                                    _ptr(mask), W, _ptr(inv_freq), _ptr(out), _ptr(ws), ws.numel(),
-                                    _stream()), "bastion_tree_attention")
-    return out
+    args = (_ptr(qkv), qkv.stride(0), S, T, Hq, Hkv, D, _ptr(k_cache), _ptr(v_cache), Lmax,
+            _ptr(ctx_len), int(max_ctx), _ptr(position_ids), _ptr(mask), W, _ptr(inv_freq),
+            _ptr(out), _ptr(ws), ws.numel(), _stream())
+    fn = L.bastion_tree_attention
+
+    def call():
+        _check(fn(*args), "bastion_tree_attention")
+
+    return out, call
 
 
 def alloc_mixture_out(B, K, b, k, device):

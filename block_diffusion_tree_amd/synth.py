@@ -72,6 +72,56 @@ WORKLOADS = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class VerifyWorkload:
+    """One attention layer of the verify pass over a batch of drafted trees:
+    S sequences, T = N + 1 tree tokens each, behind contexts drawn uniformly
+    from [ctx_lo, ctx_hi] (the contexts of the latency table below), with the
+    target's head shape (Qwen3-8B: 32 query heads, 8 KV heads of 128)."""
+
+    name: str
+    S: int
+    T: int
+    Hq: int
+    Hkv: int
+    ctx_lo: int
+    ctx_hi: int
+    seed: int
+    D: int = 128
+
+    @property
+    def lmax(self) -> int:
+        return (self.ctx_hi + self.T + 31) // 32 * 32
+
+
+VERIFY_WORKLOADS = {
+    # the trees of the main workload (64 queries, N = 64) verified in one pass
+    "verify": VerifyWorkload("verify", 64, 65, 32, 8, 512, 8192, 1006),
+}
+
+
+def make_verify_contexts(vw: VerifyWorkload) -> np.ndarray:
+    """Cached tokens per sequence, uniform on [ctx_lo, ctx_hi] (int32 [S])."""
+    rng = np.random.default_rng(vw.seed)
+    return rng.integers(vw.ctx_lo, vw.ctx_hi + 1, size=vw.S).astype(np.int32)
+
+
+def make_verify_tensors(vw: VerifyWorkload, device="cpu", seed: int | None = None):
+    """Random bf16 layer inputs: qkv rows [S*T, (Hq+2Hkv)*D] and the KV cache,
+    k [S, Hkv, Lmax, D] and v in 32-slot tiles [S, Hkv, Lmax/32, D, 32], every
+    element N(0, 1) rounded to bf16."""
+    g = _gen(vw.seed if seed is None else seed, device)
+    C = (vw.Hq + 2 * vw.Hkv) * vw.D
+    L = vw.lmax
+
+    def normal(*shape):
+        t = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        return t.normal_(0.0, 1.0, generator=g)
+
+    return (normal(vw.S * vw.T, C), normal(vw.S, vw.Hkv, L, vw.D),
+            normal(vw.S, vw.Hkv, L // 32, vw.D, 32))
+
+
 def scaled(wl: Workload, **changes) -> Workload:
     """A copy of a workload with some fields replaced (smaller parity cases)."""
     return dataclasses.replace(wl, **changes)

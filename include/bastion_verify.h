@@ -47,8 +47,8 @@ size_t bastion_tree_attention_workspace_bytes(int32_t S, int32_t T, int32_t Hq, 
  *   the call writes the tree tokens' rotated k and their v into slots
  *   ctx .. ctx+T-1, where ctx = ctx_len[s] clamped to [0, cap] with
  *   cap = max_ctx if 0 <= max_ctx < Lmax - T, else Lmax - T.  max_ctx is the
- *   caller's host-side bound of the contexts: it sizes the launch (key
- *   splits of 128 slots up to cap + T), so a tight bound saves blocks.
+ *   caller's host-side bound of the contexts: it sizes the launch (chunks of
+ *   keys up to cap + T), so a tight bound saves blocks.
  * position_ids [S][T] int32 (bastion_build_trees' pos_base + depth with
  *   pos_base = ctx): each tree token's q and k are rotated at its position:
  *   the pair (x_d, x_{d+D/2}), d < D/2, by the float32 angle
@@ -60,11 +60,16 @@ size_t bastion_tree_attention_workspace_bytes(int32_t S, int32_t T, int32_t Hq, 
  * out: bf16 [S*T][Hq*D], token-major like qkv: the attention output of
  *   q head h = kv_head * (Hq/Hkv) + g.  Scores and softmax in float32; the
  *   probabilities enter the value product rounded to bf16.
- * Limits: D = 128, Hq % Hkv == 0 with Hq/Hkv dividing 16, 1 <= T <= 1024,
+ * Limits: D = 128, Hq % Hkv == 0, 1 <= T <= 1024, S * Hq * T < 2^31,
  *   T <= Lmax <= 16384, Lmax % 32 == 0; qkv, caches and out 16-byte aligned; ws
  *   256-byte aligned with at least bastion_tree_attention_workspace_bytes.
  * Errors: EINVAL (pointers, sizes, strides, alignment), EUNSUPPORTED (D,
- *   the group size, or Lmax above 16384), EWORKSPACE.
+ *   S * Hq * T, or Lmax above 16384), EWORKSPACE.
+ * The workspace holds the rotated q rows and, for sequences whose keys span
+ *   more than one chunk, the chunks' partial outputs; the chunk length
+ *   follows from (S, Hkv, cap + T) so that the launch has about 1024 blocks
+ *   (at least 128 keys per chunk; BASTION_ATTN_BLOCKS, read once, changes
+ *   that target).
  */
 int32_t bastion_tree_attention(const void *qkv, int64_t qkv_row_stride, int32_t S, int32_t T,
                                int32_t Hq, int32_t Hkv, int32_t D, void *k_cache, void *v_cache,

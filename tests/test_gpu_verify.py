@@ -80,6 +80,8 @@ def random_parents(rng, S, T):
     (3, 33, 16, 16, 512, [0, 300, 40]),  # no grouping
     (1, 129, 16, 1, 256, [100]),         # one KV head for 16 query heads
     (2, 17, 4, 2, 96, [90, 200]),        # contexts past the cache are clamped
+    (2, 21, 6, 2, 512, [100, 7]),        # 3 query heads per KV head: tiles straddle tokens
+    (3, 1, 32, 8, 4096, [4000, 0, 37]),  # the root alone (N = 0)
 ])
 def test_tree_attention_matches_reference(S, T, Hq, Hkv, Lmax, ctx):
     rng = np.random.default_rng(T)
@@ -117,3 +119,41 @@ def test_tree_attention_consumes_build_trees_outputs():
     pos = gc.np_(g["position_ids"])
     parents = [[int(p) for p in parent[s]] for s in range(2)]
     run_case(2, T, 8, 2, 512, [333, 17], parents, seed=11, mask_pos=(mask, pos))
+
+
+def test_tree_attention_verify_workload_sampled():
+    """The benchmark's layer: the main workload's 64 trees (built by
+    bastion_build_trees from its logits, pos_base = the contexts) behind
+    contexts U[512, 8192] in an 8288-slot cache, launched as the benchmark
+    launches it (max_ctx 8192: two chunks of keys for the longer contexts);
+    the float64 reference on three sequences (the shortest context, one in
+    two chunks, the longest)."""
+    gc.require_gpu()
+    vw = synth.VERIFY_WORKLOADS["verify"]
+    wl = synth.WORKLOADS["main"]
+    ctx_np = synth.make_verify_contexts(vw)
+    ctx = torch.from_numpy(ctx_np).to("cuda")
+    x = synth.make_logits(wl, device="cuda")
+    trees = binding.build_trees(x, k=wl.k, nmax=wl.nmax, pos_base=ctx)
+    del x
+    qkv, kc, vc = synth.make_verify_tensors(vw, device="cuda")
+    inv = binding.rope_inv_freq(1.0e6, vw.D, "cuda")
+    out = binding.tree_attention(qkv, vw.S, vw.T, vw.Hq, vw.Hkv, kc, vc, ctx,
+                                 trees["position_ids"], trees["mask"], inv, max_ctx=vw.ctx_hi)
+    torch.cuda.synchronize()
+    mask = gc.np_(trees["mask"]).view(np.uint32)
+    pos = gc.np_(trees["position_ids"])
+    order = np.argsort(ctx_np)
+    pick = [int(order[0]), int(order[np.searchsorted(ctx_np[order], 4500)]), int(order[-1])]
+    T, D = vw.T, vw.D
+    for s in pick:
+        rows = qkv[s * T:(s + 1) * T].double().cpu().numpy()
+        kcs = kc[s:s + 1].double().cpu().numpy()
+        vcs = vc[s:s + 1].permute(0, 1, 3, 2, 4).reshape(1, vw.Hkv, D, vw.lmax).double().cpu().numpy()
+        ref, _, _ = vo.tree_attention(rows, 1, T, vw.Hq, vw.Hkv, D, kcs, vcs, ctx_np[s:s + 1],
+                                      pos[s:s + 1], mask[s:s + 1], inv.cpu().numpy())
+        got = out[s * T:(s + 1) * T].double().cpu().numpy()
+        vmax = max(np.abs(rows[:, (vw.Hq + vw.Hkv) * D:]).max(), np.abs(vcs).max())
+        err = np.abs(got - ref)
+        bound = 2.0 ** -8 * vmax + 2.0 ** -8 * np.abs(ref)
+        assert (err <= bound).all(), f"sequence {s} (ctx {ctx_np[s]}): max err {err.max()}"
