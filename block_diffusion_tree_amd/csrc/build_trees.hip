@@ -746,12 +746,12 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem, uint64_t *st
         F.q1n = fq1n;
         F.t0 = ft0;
         FamRegs FR;
-        const float bound = family_bound<NT>(S.qtab, S.ttab, F, b, k, kp, nmax, PL.hist, lvl, FR);
+        const float bound = family_bound<NT>(S.qtab, S.ttab, F, b, k, kp, nmax, PL.hist, lvl, FR, st);
         BASTION_STAMP(st, 5);
         // the family usually holds every node at or above the bound; if not,
         // one wave enumerates them level by level
         const int nf = family_select<NT>(PL, S.qtab, S.ttab, F, FW, FR, b, k, kp, bound,
-                                               kPoolCap, lvl);
+                                               kPoolCap, lvl, st);
         BASTION_STAMP(st, 6);
         if (nf >= 1 && nf <= kPoolCap) {
             FamGeom FG;
@@ -768,7 +768,7 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem, uint64_t *st
             FG.ttab = S.ttab;
             FG.cmask = FW.cmask;
             FG.gpre = FW.gpre;
-            cnt = family_rank<NT>(PL, FG, nf, nmax, kPoolCap, S.par, S.dep, S.tok, S.rho);
+            cnt = family_rank<NT>(PL, FG, nf, nmax, kPoolCap, S.par, S.dep, S.tok, S.rho, st);
         } else if (nf == -1) {
             if (wv == 0) {
                 const int n = pool_enumerate(PL, S.qtab, S.ttab, b, k, kp, bound, kPoolCap);

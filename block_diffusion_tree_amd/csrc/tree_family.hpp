@@ -133,7 +133,9 @@ struct FamRegs {
 template <int THREADS>
 __device__ __forceinline__ float family_bound(const float *qtab, const int32_t *ttab,
                                               const FamilyCols &F, int b, int k, int kp, int n,
-                                              uint32_t *hist, float *lvl, FamRegs &R) {
+                                              uint32_t *hist, float *lvl, FamRegs &R,
+                                              uint64_t *st = nullptr) {
+    (void)st;
     constexpr int W = THREADS / kWave;
     const int tid = threadIdx.x, lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -161,6 +163,7 @@ __device__ __forceinline__ float family_bound(const float *qtab, const int32_t *
         prev = off;
         off += sz;
     }
+    BASTION_STAMP(st, 10);
     // deeper than D: the top-1 path and the paths leaving it once
     if (D < b) {
         const int npair = b * (k - 1);
@@ -212,6 +215,7 @@ __device__ __forceinline__ float family_bound(const float *qtab, const int32_t *
         }
     }
     __syncthreads();
+    BASTION_STAMP(st, 11);
     // lane l owns bins 1008-16l .. 1023-16l; cb[15] is its highest
     const pool_u32x4 *h4 = reinterpret_cast<const pool_u32x4 *>(hist + (kHistBins - 16 - 16 * lane));
     uint32_t cb[16], own = 0;
@@ -255,7 +259,9 @@ __device__ __forceinline__ float family_bound(const float *qtab, const int32_t *
 template <int THREADS>
 __device__ int family_select(const PoolLds &L, const float *qtab, const int32_t *ttab,
                              const FamilyCols &F, const FamilyWork &Wk, const FamRegs &R, int b,
-                             int k, int kp, float t, int cap, const float *lvl) {
+                             int k, int kp, float t, int cap, const float *lvl,
+                             uint64_t *st = nullptr) {
+    (void)st;
     constexpr int W = THREADS / kWave, MC = kFamilyLevels / THREADS;
     static_assert(kFamilyLevels % THREADS == 0 && MC * W == kFamGroups, "family groups");
     const int tid = threadIdx.x, lane = lane_id();
@@ -365,6 +371,7 @@ __device__ int family_select(const PoolLds &L, const float *qtab, const int32_t 
     }
     if (esc) Wk.flag[0] = 1;
     __syncthreads();
+    BASTION_STAMP(st, 12);
     if (Wk.flag[0] != 0) return -1;
 
     // slot bases: complete nodes by group prefix, paths by (round, wave)
@@ -543,7 +550,9 @@ __device__ __forceinline__ int fam_parent(const FamGeom &G, uint64_t x, int s) {
 // nodes past cnt) and returns cnt.
 template <int THREADS>
 __device__ int family_rank(const PoolLds &L, const FamGeom &G, int n, int nmax, int cap,
-                           int32_t *par, int32_t *dep, int32_t *tok, float *rho) {
+                           int32_t *par, int32_t *dep, int32_t *tok, float *rho,
+                           uint64_t *st = nullptr) {
+    (void)st;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     n = __builtin_amdgcn_readfirstlane(n);
     // task = (node e, part of the keys): P parts per node, as many as the
@@ -593,6 +602,7 @@ __device__ int family_rank(const PoolLds &L, const FamGeom &G, int n, int nmax, 
         atomicAdd(L.pop + (ve ? e : cap + kPoolPad + lane), gt);
     }
     __syncthreads();
+    BASTION_STAMP(st, 13);
     const int cnt = n < nmax ? n : nmax;
     for (int e = tid; e < n; e += THREADS) {
         const int pe = L.pop[e] + 1;

@@ -24,6 +24,12 @@ SLOTS = 16
 TREE_PHASES = [(3, 4, "load rows' top-k and status"), (4, 5, "family bound"),
                (5, 6, "family select"), (6, 7, "rank (or pool / exact build)"),
                (7, 8, "A_hat, online stop"), (8, 9, "emission (tree, mask, positions)")]
+# finer stamps inside the family bound, select and rank (slots 10-13; a
+# query whose pool leaves the family skips some of them)
+SUB_PHASES = [(4, 10, "bound: complete levels"), (10, 11, "bound: paths, histogram"),
+              (11, 5, "bound: histogram scan"), (5, 12, "select: masks, path counts"),
+              (12, 6, "select: slot writes"), (6, 13, "rank: counts"),
+              (13, 7, "rank: parents, records")]
 
 
 def run(workload: str, reps: int, split: int):
@@ -95,13 +101,16 @@ def analyse(wl, st):
     end_slot = 9
     last = trees[np.argmax(trees[:, end_slot])]
     out["kernel_end"] = float(us(trees[:, end_slot]).max())
-    out["last_tree"] = {name: float((last[b] - last[a]) / 100.0) for a, b, name in TREE_PHASES
-                        if last[a] and last[b]}
+    out["last_tree"] = {name: float((last[b] - last[a]) / 100.0)
+                        for a, b, name in TREE_PHASES + SUB_PHASES if last[a] and last[b]}
     out["last_tree_start"] = float(us(np.array([last[3]]))[0])
     out["tree_total_p50"] = float(np.median((trees[:, end_slot] - trees[:, 3]) / 100.0))
     # per-phase medians over every tree
-    out["phase_p50"] = {name: float(np.median((trees[:, b] - trees[:, a]) / 100.0))
-                        for a, b, name in TREE_PHASES if (trees[:, a] != 0).all() and (trees[:, b] != 0).all()}
+    out["phase_p50"] = {}
+    for a, b, name in TREE_PHASES + SUB_PHASES:
+        ok = (trees[:, a] != 0) & (trees[:, b] != 0)
+        if ok.any():
+            out["phase_p50"][name] = float(np.median((trees[ok, b] - trees[ok, a]) / 100.0))
     return out
 
 
@@ -131,11 +140,11 @@ def main():
           " / ".join(f"{med(lambda r, i=i: r['quarter_p50'][i]):.1f}" for i in range(4)) + " |")
     print(f"| last row finished after the last stream end | {med(lambda r: r['merge_gap']):.1f} |")
     print(f"| tree stage of the last query: start | {med(lambda r: r['last_tree_start']):.1f} |")
-    for _, _, name in TREE_PHASES:
+    for _, _, name in TREE_PHASES + SUB_PHASES:
         v = med(lambda r, n=name: r["last_tree"].get(n, np.nan))
         print(f"| ... {name} | {v:.2f} |")
     print(f"| tree stage duration, p50 over queries | {med(lambda r: r['tree_total_p50']):.1f} |")
-    for _, _, name in TREE_PHASES:
+    for _, _, name in TREE_PHASES + SUB_PHASES:
         v = med(lambda r, n=name: r["phase_p50"].get(n, np.nan))
         print(f"| ... p50 over queries: {name} | {v:.2f} |")
 
