@@ -66,13 +66,20 @@ def parse():
     return ap.parse_args()
 
 
+# the sources the tree and mixture launches are built from (kernels, their
+# headers and the launch plan); counter readings taken on other versions of
+# them are stale
+TREE_PATH_SOURCES = ["api.hip", "api_internal.hpp", "build_trees.hip", "build_params.hpp",
+                     "device_common.hpp", "mixture.hpp", "tree_family.hpp", "tree_pool.hpp",
+                     "tree_rounds.hpp"]
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources; counter readings taken on other sources are stale."""
-    import glob
+    """Hash of the tree path's HIP sources and its header."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     csrc = os.path.join(root, "block_diffusion_tree_amd", "csrc")
-    files = sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp")))
+    files = [os.path.join(csrc, f) for f in TREE_PATH_SOURCES]
     files.append(os.path.join(root, "include", "bastion.h"))
     h = hashlib.sha256()
     for f in files:
