@@ -29,8 +29,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kThreads = 256;               // 4 waves
 constexpr int kWavesPerBlock = kThreads / kWave;
 constexpr int kCap = 256;                   // per-wave candidate buffer (keys)
-
-
+#ifndef BASTION_FUSED_STAGED
+#define BASTION_FUSED_STAGED 0
+#endif
+// the staged online build (tree_stage) in the trees of the stream launch too
+constexpr bool kFusedStaged = BASTION_FUSED_STAGED != 0;
 
 // storage-type traits ------------------------------------------------------
 template <typename T> struct Elem;
@@ -316,16 +319,13 @@ __device__ SegmentResult stream_segment(const BuildParams &P, const char *row, i
         // The instruction arbiter favours older waves, so the blocks sharing
         // a CU would otherwise finish one after another and leave the CU
         // with a single streaming block at the end.  A wave's priority falls
-        // as its segment progresses, which keeps the co-resident blocks
-        // level; in a grid that is resident at once (at most four blocks per
-        // CU), blocks dispatched later (the grid is dispatched in order, over
-        // several microseconds) keep a higher priority for longer, by one
-        // tier per quarter of the grid.
-        const int age = int(gridDim.x) <= P.resident_blocks ? int((blockIdx.x * 4u) / gridDim.x) : 0;
+        // as its segment progresses (four tiers), which keeps the
+        // co-resident blocks level.  (A later start for blocks dispatched
+        // later, one tier per quarter of the grid, measured 1.2 us slower at
+        // the 64 x 16 x 151936 bf16 workload.)
         int tier = -1;
         for (int t = 0; t < ntot; t += 2) {
-            int nt = (4 * t) / ntot - age;
-            nt = nt < 0 ? 0 : nt;
+            const int nt = (4 * t) / ntot;
             if (nt != tier) {
                 tier = nt;
                 if (nt == 0) __builtin_amdgcn_s_setprio(3);
@@ -656,7 +656,7 @@ __device__ void emit_tree(const BuildParams &P, int q, const int32_t *par, const
 }
 
 // st: this block's timestamps (stamped build), or null
-template <int G, int NT = kThreads>
+template <int G, int NT = kThreads, bool STAGED = false>
 __device__ void tree_stage(const BuildParams &P, int q, char *smem, uint64_t *st) {
     (void)st;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -730,91 +730,145 @@ __device__ void tree_stage(const BuildParams &P, int q, char *smem, uint64_t *st
     // a bad row outranks a row outside the float32 range
     const int bad_status = (s_bad & 1) ? BASTION_Q_BAD_LOGITS : BASTION_Q_RANGE;
 
-    __shared__ int s_pool;
-    int cnt = -1;
+    __shared__ int s_pool, s_pass, s_more;
+    // Online stop, staged: best-first trees of budgets n1 < nmax are
+    // prefixes of one another (same pop order, same A_hat sums), so if the
+    // stop falls inside the first n1 = kStageNodes nodes, the tree of budget
+    // n1 is the answer and the full budget is never ranked.  The first stage
+    // is skipped when no stop can fall inside it: with at least n1 real
+    // nodes at rho >= t1 (the family's bound for n1 nodes), rho(n+1) >= t1
+    // and A_hat(n) <= 1 + n rho_1 for n < n1, so S cannot fall while
+    // t1 C(n) >= (1 + n rho_1) (C(n+1) - C(n)).
+    constexpr int kStageNodes = 32;
+    const bool staged = STAGED && online && nmax > kStageNodes;
+    PoolLds PL;
+    FamilyCols F;
+    FamRegs FR;
+    float *lvl = nullptr;
+    float bound = 0.0f, bound1 = 0.0f;
     if (kPoolCap > 0 && !bad) {
-        PoolLds PL;
         PL.key = reinterpret_cast<uint64_t *>(smem + TL.pkey);
         PL.par = reinterpret_cast<int32_t *>(smem + TL.ppar);
         PL.rho = reinterpret_cast<float *>(smem + TL.prho);
         PL.lrank = reinterpret_cast<int32_t *>(smem + TL.plrank);
         PL.pop = reinterpret_cast<int32_t *>(smem + TL.ppop);
         PL.hist = reinterpret_cast<uint32_t *>(smem + TL.hist);
-        float *lvl = reinterpret_cast<float *>(smem + TL.plvl);
-        FamilyCols F;
+        lvl = reinterpret_cast<float *>(smem + TL.plvl);
         F.q0 = fq0;
         F.q1n = fq1n;
         F.t0 = ft0;
-        FamRegs FR;
-        const float bound = family_bound<NT>(S.qtab, S.ttab, F, b, k, kp, nmax, PL.hist, lvl, FR, st);
+        bound = family_bound<NT>(S.qtab, S.ttab, F, b, k, kp, nmax, PL.hist, lvl, FR, st,
+                                 staged ? kStageNodes : 0, &bound1);
         BASTION_STAMP(st, 5);
-        // the family usually holds every node at or above the bound; if not,
-        // one wave enumerates them level by level
-        const int nf = family_select<NT>(PL, S.qtab, S.ttab, F, FW, FR, b, k, kp, bound,
-                                               kPoolCap, lvl, st);
-        BASTION_STAMP(st, 6);
-        if (nf >= 1 && nf <= kPoolCap) {
-            FamGeom FG;
-            int tot;
-            FG.D = family_depth(b, k, tot);
-            int kD = 1;
-            for (int x = 0; x < FG.D; ++x) kD *= k;
-            FG.k = k;
-            FG.kp = kp;
-            FG.firstD = tot - kD;
-            FG.topbase = FW.flag[3];
-            FG.inv_k = (65536u + uint32_t(k) - 1u) / uint32_t(k);
-            FG.lvl = lvl;
-            FG.ttab = S.ttab;
-            FG.cmask = FW.cmask;
-            FG.gpre = FW.gpre;
-            cnt = family_rank<NT>(PL, FG, nf, nmax, kPoolCap, S.par, S.dep, S.tok, S.rho, st);
-        } else if (nf == -1) {
-            if (wv == 0) {
-                const int n = pool_enumerate(PL, S.qtab, S.ttab, b, k, kp, bound, kPoolCap);
-                if (lane == 0) s_pool = n;
+    }
+    // pass 0 is the first stage, pass 1 the whole budget
+    int pass0 = 1;
+    if (staged) {
+        if (tid == 0) s_pass = 1;
+        if (!bad && wv == 0) {
+            // stage one unless the certificate holds for every n in [nmin, n1)
+            const float rho1 = S.qtab[0];
+            bool may_stop = !(bound1 > 0.0f);
+            for (int n = P.nmin + lane; n < kStageNodes && !may_stop; n += kWave) {
+                const double dc = S.cost[n + 1] - S.cost[n];
+                may_stop = double(bound1) * S.cost[n] < (1.0 + double(n) * rho1) * (dc > 0.0 ? dc : 0.0);
             }
-            __syncthreads();
-            const int n = s_pool;
-            if (n >= 1) cnt = pool_rank<NT>(PL, n, nmax, S.par, S.dep, S.tok, S.rho);
+            const bool any = __ballot(may_stop) != 0;
+            if (lane == 0) s_pass = any ? 0 : 1;
         }
         __syncthreads();
+        pass0 = s_pass;
     }
 
-    BASTION_STAMP(st, 7);
-    if (!bad && wv == 0) {
-        if (cnt < 0) cnt = exact_build<G>(S, b, k, nmax);
-        if (lane == 0) {
-            S.par[0] = -1;
-            S.dep[0] = 0;
-            S.tok[0] = -1;
-            S.rho[0] = 1.0f;
-            S.ahat[0] = 1.0;
-        }
-        wave_sync();
-        ahat_fill(S.rho, S.ahat, cnt);
-        int nstar = cnt;
-        if (online) {
-            // the first n >= nmin with S(n+1) < S(n)
-            for (int c0 = 0; c0 < cnt; c0 += kWave) {
-                const int n = c0 + lane;
-                bool dec = false;
-                if (n < cnt && n >= P.nmin) {
-                    const double s0 = (S.ahat[n] * P.l_ar) / S.cost[n];
-                    const double s1 = (S.ahat[n + 1] * P.l_ar) / S.cost[n + 1];
-                    dec = s1 < s0;
+    for (int pass = pass0; pass < 2; ++pass) {
+        // the best-first tree of budget N from the pool of nodes at or above
+        // t (the exact build when there is no pool), its A_hat and the stop
+        const int N = pass == 0 ? kStageNodes : nmax;
+        int cnt = -1;
+        if (kPoolCap > 0 && !bad) {
+            const float t = pass == 0 ? bound1 : bound;
+            if (pass > pass0) {
+                // the second stage starts from the pool state of the first
+                int32_t *pop = reinterpret_cast<int32_t *>(smem + TL.ppop);
+                for (int i = tid; i < kPoolCap + kPoolPad + kWave; i += NT) pop[i] = 0;
+                if (tid == 0) FW.flag[0] = 0;
+                __syncthreads();
+            }
+            // the family usually holds every node at or above the bound; if
+            // not, one wave enumerates them level by level
+            const int nf = family_select<NT>(PL, S.qtab, S.ttab, F, FW, FR, b, k, kp, t,
+                                             kPoolCap, lvl, st);
+            BASTION_STAMP(st, 6);
+            if (nf >= 1 && nf <= kPoolCap) {
+                FamGeom FG;
+                int tot;
+                FG.D = family_depth(b, k, tot);
+                int kD = 1;
+                for (int x = 0; x < FG.D; ++x) kD *= k;
+                FG.k = k;
+                FG.kp = kp;
+                FG.firstD = tot - kD;
+                FG.topbase = FW.flag[3];
+                FG.inv_k = (65536u + uint32_t(k) - 1u) / uint32_t(k);
+                FG.lvl = lvl;
+                FG.ttab = S.ttab;
+                FG.cmask = FW.cmask;
+                FG.gpre = FW.gpre;
+                cnt = family_rank<NT>(PL, FG, nf, N, kPoolCap, S.par, S.dep, S.tok, S.rho, st);
+            } else if (nf == -1) {
+                if (wv == 0) {
+                    const int n = pool_enumerate(PL, S.qtab, S.ttab, b, k, kp, t, kPoolCap);
+                    if (lane == 0) s_pool = n;
                 }
-                const uint64_t msk = __ballot(dec);
-                if (msk) {
-                    nstar = c0 + __ffsll((unsigned long long)msk) - 1;
-                    break;
+                __syncthreads();
+                const int n = s_pool;
+                if (n >= 1) cnt = pool_rank<NT>(PL, n, N, S.par, S.dep, S.tok, S.rho);
+            }
+            __syncthreads();
+        }
+
+        BASTION_STAMP(st, 7);
+        if (!bad && wv == 0) {
+            if (cnt < 0) cnt = exact_build<G>(S, b, k, N);
+            if (lane == 0) {
+                S.par[0] = -1;
+                S.dep[0] = 0;
+                S.tok[0] = -1;
+                S.rho[0] = 1.0f;
+                S.ahat[0] = 1.0;
+            }
+            wave_sync();
+            ahat_fill(S.rho, S.ahat, cnt);
+            int nstar = cnt;
+            bool found = false;
+            if (online) {
+                // the first n >= nmin with S(n+1) < S(n)
+                for (int c0 = 0; c0 < cnt; c0 += kWave) {
+                    const int n = c0 + lane;
+                    bool dec = false;
+                    if (n < cnt && n >= P.nmin) {
+                        const double s0 = (S.ahat[n] * P.l_ar) / S.cost[n];
+                        const double s1 = (S.ahat[n + 1] * P.l_ar) / S.cost[n + 1];
+                        dec = s1 < s0;
+                    }
+                    const uint64_t msk = __ballot(dec);
+                    if (msk) {
+                        nstar = c0 + __ffsll((unsigned long long)msk) - 1;
+                        found = true;
+                        break;
+                    }
                 }
             }
+            if (lane == 0) {
+                s_nstar = nstar;
+                s_status = (nstar == cnt && cnt < nmax) ? BASTION_Q_EXHAUSTED : BASTION_Q_OK;
+                // the first stage decides only a stop inside it or a tree
+                // that ended before its budget
+                s_more = (pass == 0 && !found && cnt == N) ? 1 : 0;
+            }
         }
-        if (lane == 0) {
-            s_nstar = nstar;
-            s_status = (nstar == cnt && cnt < nmax) ? BASTION_Q_EXHAUSTED : BASTION_Q_OK;
-        }
+        __syncthreads();
+        if (!staged || bad || s_more == 0) break;
     }
     __syncthreads();
     BASTION_STAMP(st, 8);
@@ -1277,7 +1331,7 @@ __global__ __launch_bounds__(kThreads, (R >= 16 ? 2 : 4)) void build_trees_kerne
     // them (a finished stream leaves this block's waves at priority 0).
     __builtin_amdgcn_s_setprio(3);
     BASTION_STAMP(P.stamps, 3);
-    tree_stage<R>(P, q, smem, P.stamps);
+    tree_stage<R, kThreads, kFusedStaged>(P, q, smem, P.stamps);
 }
 
 // ---------------------------------------------------------------------------
@@ -1443,18 +1497,18 @@ __global__ __launch_bounds__(kMixThreads) void mixture_kernel(BuildParams P) {
 // one block per query, launched after the stream kernel on the same stream.
 // Run by the last row block of a query inside the stream grid, a tree would
 // hold a block slot while rows of later queries wait to be dispatched.
-// The block has a CU to itself, so it takes 16 waves (8 with the largest
+// The block has a CU to itself, so it takes 16 waves (8 with the two largest
 // running lists, whose registers would not fit 16): the stage's comparison
 // and walk loops are latency-bound at one wave per SIMD.
 template <int R>
-constexpr int tree_threads() { return R >= 16 ? 512 : 1024; }
+constexpr int tree_threads() { return R >= 8 ? 512 : 1024; }
 
 template <int R>
 __global__ __launch_bounds__(tree_threads<R>()) void tree_kernel(BuildParams P) {
     extern __shared__ __align__(16) char smem[];
     uint64_t *st = P.stamps ? P.stamps + P.stamp_second * kStampSlots : nullptr;
     BASTION_STAMP(st, 3);
-    tree_stage<R, tree_threads<R>()>(P, int(blockIdx.x), smem, st);
+    tree_stage<R, tree_threads<R>(), true>(P, int(blockIdx.x), smem, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -129,12 +129,14 @@ struct FamRegs {
 // Step 1, by the whole block.  hist (kHistBins + kWave bins) must be zero
 // and visible to the block.  Writes the complete levels' rho to lvl[0, tot).
 // Returns the lower bound t (every wave reads the histogram itself), 0 when
-// the family holds fewer than n nodes.
+// the family holds fewer than n nodes; with bound2, also the bound of n2
+// nodes.
 template <int THREADS>
 __device__ __forceinline__ float family_bound(const float *qtab, const int32_t *ttab,
                                               const FamilyCols &F, int b, int k, int kp, int n,
                                               uint32_t *hist, float *lvl, FamRegs &R,
-                                              uint64_t *st = nullptr) {
+                                              uint64_t *st = nullptr, int n2 = 0,
+                                              float *bound2 = nullptr) {
     (void)st;
     constexpr int W = THREADS / kWave;
     const int tid = threadIdx.x, lane = lane_id();
@@ -230,21 +232,29 @@ __device__ __forceinline__ float family_bound(const float *qtab, const int32_t *
 #pragma unroll
     for (int i = 0; i < 16; ++i) own += cb[i];
     const uint32_t incl = wave_incl_scan_u32(own);
-    const uint64_t reach = __ballot(incl >= uint32_t(n));
-    if (reach == 0) return 0.0f;
-    const int l = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)reach) - 1);
-    int bin = kHistBins - 16 - 16 * lane;
+    // The lower edge of the first bin (from the top) where the count reaches
+    // m; 0 when the family holds fewer than m nodes.  The count from the top
+    // grows toward a lane's lower bins, so on the first lane whose inclusive
+    // count reaches m the bin is 15 - (its bins still below m) in its block.
+    const uint32_t m1 = uint32_t(n), m2 = uint32_t(n2 >= 1 ? n2 : n);
     uint32_t acc = incl - own;
-    bool found = false;
+    int below1 = 0, below2 = 0;
 #pragma unroll
     for (int i = 15; i >= 0; --i) {
         acc += cb[i];
-        const bool hit = !found && acc >= uint32_t(n);
-        bin = hit ? kHistBins - 16 - 16 * lane + i : bin;
-        found = found || hit;
+        below1 += acc < m1 ? 1 : 0;
+        below2 += acc < m2 ? 1 : 0;
     }
-    bin = __builtin_amdgcn_readlane(bin, l);
-    return __uint_as_float(uint32_t(bin) << 20);
+    const int base = kHistBins - 1 - 16 * lane;
+    auto edge = [&](uint32_t m, int below) -> float {
+        const uint64_t reach = __ballot(incl >= m);
+        if (reach == 0) return 0.0f;
+        const int l = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)reach) - 1);
+        const int bin = __builtin_amdgcn_readlane(base - below, l);
+        return __uint_as_float(uint32_t(bin) << 20);
+    };
+    if (bound2) *bound2 = n2 >= 1 ? edge(m2, below2) : 0.0f;
+    return edge(m1, below1);
 }
 
 // Step 2, by the whole block, after family_bound (lvl holds the complete

@@ -96,6 +96,34 @@ def test_sweep_logits_with_peaks_online():
     assert n.min() > 4 and n.max() < 256
 
 
+@pytest.mark.parametrize("launch", ["stream", "own"])
+def test_online_stop_around_the_first_stage(launch):
+    """Cost tables shaped so that the stop falls before, on and after the
+    32-node first stage of a budget-256 online build, or never; half of the
+    rows add a small cost step after one node, large enough that the first
+    stage cannot be ruled out in advance but too small to stop there.  The
+    trees built in the stream launch and in their own launch."""
+    binding.set_tuning(split_trees=1 if launch == "own" else 0)
+    wl = synth.scaled(synth.WORKLOADS["main"], B=12, V=32000, nmax=256, seed=1011)
+    x = gc.device_logits(wl)
+    ref = oracle.softmax_topk(oracle.host_logits(x), k=wl.k)
+    fixed = oracle.best_first(ref["topk_ids"], ref["topk_p"].astype(np.float32), nmax=wl.nmax)
+    plan = [(1, False), (5, False), (30, False), (31, False), (32, False), (33, False),
+            (100, False), (None, False), (5, True), (31, True), (33, True), (None, True)]
+    cost = np.ones((wl.B, wl.nmax + 1))
+    for r, (m, bump) in enumerate(plan):
+        if bump:
+            rho = fixed["rho"][r].astype(np.float64)
+            # (1 + rho_1) * step lies between rho_32 and rho_2: no stop at
+            # one node, while the stop test there is not ruled out by rho_32
+            cost[r, 2:] += np.sqrt(rho[32] * rho[2]) / (1.0 + rho[1])
+        if m is not None:
+            cost[r, m + 1:] = 1.0e6
+    g, _ = gc.run_and_check(x, wl.k, wl.nmax, nmin=1, cost=torch.from_numpy(cost).to("cuda"))
+    want = [wl.nmax if m is None else m for m, _ in plan]
+    assert gc.np_(g["n_nodes"]).tolist() == want
+
+
 def test_trees_in_their_own_launch():
     """Stream grids larger than the machine (here 1280 rows) build the trees
     in a launch of their own, with the online budget stop."""
