@@ -68,6 +68,20 @@ struct WaveScratch {
     uint64_t cand[kCap];
 };
 
+// Block merge of the waves' candidate keys (each wave's list in its own
+// scratch, at most 64 keys, counts in n[]), by wave 0: the k best in
+// descending order into scr[0].cand; returns their number.  lb: a key that
+// at least min(k, all keys) of them reach.
+template <int U>
+__device__ __forceinline__ int block_topk(WaveScratch<U> *scr, const int *n, int k, uint64_t lb,
+                                          uint64_t &kth) {
+    const int lane = __lane_id();
+    uint64_t kv[kThreads / kWave];
+#pragma unroll
+    for (int w = 0; w < kThreads / kWave; ++w) kv[w] = lane < n[w] ? scr[w].cand[lane] : 0;
+    return wave_topk_keys<kThreads / kWave>(kv, k, lb, scr[0].cand, kth);
+}
+
 // ---------------------------------------------------------------------------
 // Per-wave state of the streaming stage.
 // ---------------------------------------------------------------------------
@@ -93,7 +107,7 @@ struct Streamer {
 
     __device__ void compact() {
         uint64_t kth;
-        cnt = wave_select_topk<kCap / kWave>(ws->cand, cnt, k, kth);
+        cnt = wave_select_topk<kCap / kWave, true>(ws->cand, cnt, k, kth);
         if (kth > thk) {
             thk = kth;
             thv = topk_key_value(kth);
@@ -252,7 +266,7 @@ struct SegmentResult {
 };
 
 template <typename T, int U>
-__device__ SegmentResult stream_segment(const BuildParams &P, const char *row, int seg, char *smem) {
+__device__ __forceinline__ SegmentResult stream_segment(const BuildParams &P, const char *row, int seg, char *smem) {
     constexpr int E = Elem<T>::kPerVec;
     constexpr int ES = int(sizeof(T));
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -386,17 +400,10 @@ __device__ SegmentResult stream_segment(const BuildParams &P, const char *row, i
         Ssum += red_s[i] * __builtin_amdgcn_exp2f(scale_ref(red_m[i]) - C);
     res.m = M;
     res.s = Ssum;
-    // ---- block merge: top-k (wave 0 gathers the other waves' keys) ----
+    // ---- block merge: top-k (wave 0), bounded below by the block threshold ----
     if (wv == 0) {
-        int total = red_n[0];
-        for (int w = 1; w < kWavesPerBlock; ++w) {
-            const int nw = red_n[w];
-            if (lane < nw) scr[0].cand[total + lane] = scr[w].cand[lane];
-            total += nw;
-        }
-        wave_sync();
         uint64_t kth;
-        res.nsel = wave_select_topk<kCap / kWave>(scr[0].cand, total, P.k, kth);
+        res.nsel = block_topk<U>(scr, red_n, P.k, s_bth, kth);
     }
     return res;  // res.nsel valid in wave 0 only
 }
@@ -418,7 +425,7 @@ __device__ __forceinline__ V ld_agent(const V *p) {
     return __hip_atomic_load(const_cast<V *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ bool arrive_last(uint32_t *ticket, uint32_t total) {
+__device__ __forceinline__ bool arrive_last(uint32_t *ticket, uint32_t total) {
     __shared__ int flag;
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's stores are done
     __syncthreads();
@@ -657,7 +664,7 @@ __device__ void emit_tree(const BuildParams &P, int q, const int32_t *par, const
 
 // st: this block's timestamps (stamped build), or null
 template <int G, int NT = kThreads, bool STAGED = false>
-__device__ void tree_stage(const BuildParams &P, int q, char *smem, uint64_t *st) {
+__device__ __forceinline__ void tree_stage(const BuildParams &P, int q, char *smem, uint64_t *st) {
     (void)st;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const TreeLayout TL = tree_layout(P.b, P.k, P.nmax, NT);
@@ -1264,28 +1271,47 @@ __global__ __launch_bounds__(kThreads, (R >= 16 ? 2 : 4)) void build_trees_kerne
                 ls += ld_agent(r + 1) * __builtin_amdgcn_exp2f(scale_ref(ld_agent(r)) - C);
             }
             Ssum = wave_sum_f32(ls);
-            // keys: append with the same capacity/compaction rule as the stream
-            int cnt = 0;
-            uint64_t thk = 0, kth;
+            uint64_t kth;
             const int tot = P.S * P.k;
-            for (int e0 = 0; e0 < tot; e0 += kWave) {
-                if (cnt + kWave > kCap) {
-                    cnt = wave_select_topk<kCap / kWave>(cand, cnt, P.k, kth);
-                    thk = kth;
+            constexpr int kRegKeys = kCap / kWave;
+            if (tot <= kRegKeys * kWave) {
+                // every record's keys in registers, loaded at once; a record
+                // with k keys bounds the row's k-th best by its last one
+                uint64_t kv[kRegKeys], last = 0;
+#pragma unroll
+                for (int i = 0; i < kRegKeys; ++i) {
+                    const int e = i * kWave + lane;
+                    const int sg = e / P.k, j = e - sg * P.k;
+                    kv[i] = e < tot ? ld_agent(reinterpret_cast<const uint64_t *>(
+                                                   base + int64_t(sg) * P.partial_bytes + 16) + j)
+                                    : uint64_t(0);
+                    if (e < tot && j == P.k - 1 && kv[i] > last) last = kv[i];
                 }
-                const int e = e0 + lane;
-                uint64_t key = 0;
-                if (e < tot) {
-                    const int s = e / P.k, j = e - s * P.k;
-                    key = ld_agent(reinterpret_cast<const uint64_t *>(base + int64_t(s) * P.partial_bytes + 16) + j);
+                nsel = wave_topk_keys<kRegKeys>(kv, P.k, wave_max_u64(last), cand, kth);
+            } else {
+                // keys: append with the same capacity/compaction rule as the stream
+                int cnt = 0;
+                uint64_t thk = 0;
+                for (int e0 = 0; e0 < tot; e0 += kWave) {
+                    if (cnt + kWave > kCap) {
+                        cnt = wave_select_topk<kCap / kWave>(cand, cnt, P.k, kth);
+                        thk = kth;
+                    }
+                    const int e = e0 + lane;
+                    uint64_t key = 0;
+                    if (e < tot) {
+                        const int s = e / P.k, j = e - s * P.k;
+                        key = ld_agent(reinterpret_cast<const uint64_t *>(
+                                           base + int64_t(s) * P.partial_bytes + 16) + j);
+                    }
+                    const bool p = key != 0 && key > thk;
+                    const uint64_t msk = __ballot(p);
+                    if (p) cand[cnt + popc64(msk & lanemask_lt())] = key;
+                    cnt += popc64(msk);
+                    wave_sync();
                 }
-                const bool p = key != 0 && key > thk;
-                const uint64_t msk = __ballot(p);
-                if (p) cand[cnt + popc64(msk & lanemask_lt())] = key;
-                cnt += popc64(msk);
-                wave_sync();
+                nsel = wave_select_topk<kCap / kWave>(cand, cnt, P.k, kth);
             }
-            nsel = wave_select_topk<kCap / kWave>(cand, cnt, P.k, kth);
         }
     }
     // ---- finish the row (wave 0) ----
@@ -1453,15 +1479,8 @@ __global__ __launch_bounds__(kThreads) void marginal_kernel(BuildParams P) {
     if (lane == 0) red_n[wv] = st.cnt;
     __syncthreads();
     if (wv == 0) {
-        int total = red_n[0];
-        for (int w = 1; w < kWavesPerBlock; ++w) {
-            const int nw = red_n[w];
-            if (lane < nw) scr[0].cand[total + lane] = scr[w].cand[lane];
-            total += nw;
-        }
-        wave_sync();
         uint64_t kth;
-        const int nsel = wave_select_topk<kCap / kWave>(scr[0].cand, total, k, kth);
+        const int nsel = block_topk<U>(scr, red_n, k, *st.bth, kth);
         if (lane < k) {
             const uint64_t key = lane < nsel ? scr[0].cand[lane] : 0;
             const int tok = lane < nsel ? topk_key_token(key) : -1;

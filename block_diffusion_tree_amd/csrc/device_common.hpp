@@ -228,39 +228,144 @@ __device__ __forceinline__ float scale_ref(float m) {
     return fmaxf(m * kLog2e, -3.402823466e38f);
 }
 
+// Number of the keys (all lanes, all registers) at or above t.
+template <int PER_LANE>
+__device__ __forceinline__ int count_ge(const uint64_t (&kv)[PER_LANE], uint64_t t) {
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) c += popc64(__ballot(kv[i] >= t));
+    return c;
+}
+
+// Top-k by k rounds of a wave argmax, with the contract of wave_topk_keys
+// below: less code, and for k <= 4 less time than its search.
+template <int PER_LANE>
+__device__ __forceinline__ int wave_rounds_topk(const uint64_t (&kv)[PER_LANE], int k,
+                                                uint64_t *cand, uint64_t &kth) {
+    const int lane = lane_id();
+    const int count = count_ge(kv, 1);
+    const int nsel = count < k ? count : k;
+    uint64_t w[PER_LANE];
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) w[i] = kv[i];
+    uint64_t mine = 0;
+    kth = 0;
+    for (int r = 0; r < nsel; ++r) {
+        uint64_t lm = w[0];
+#pragma unroll
+        for (int i = 1; i < PER_LANE; ++i) lm = w[i] > lm ? w[i] : lm;
+        const uint64_t wm = wave_max_u64(lm);
+#pragma unroll
+        for (int i = 0; i < PER_LANE; ++i) w[i] = w[i] == wm ? 0 : w[i];
+        if (lane == r) mine = wm;
+        if (r == k - 1) kth = wm;
+    }
+    wave_sync();
+    if (lane < nsel) cand[lane] = mine;
+    wave_sync();
+    return nsel;
+}
+
 // ---------------------------------------------------------------------------
-// Top-k selection inside one wave.  `cand` (LDS) holds `count` unique keys;
-// afterwards cand[0..min(k,count)) holds the best of them in descending
-// order and the function returns that number.  `kth` receives the k-th key
-// (0 when fewer than k keys exist).  Work: k rounds of a wave argmax over
-// ceil(count/64) keys per lane.
+// Top-k selection inside one wave (k <= 32).  The candidate keys are unique
+// and nonzero; kv[i] of lane l holds one of them or 0, PER_LANE per lane.
+// Afterwards cand[0..nsel) (LDS, at least 64 slots) holds the best
+// nsel = min(k, number of keys) in descending order, and kth the k-th best
+// key (0 when there are fewer than k).  lb: a key that at least nsel of the
+// keys reach (0 when none is known).
+//
+// A threshold T with k <= #{keys >= T} <= cap is found by bisecting the key
+// range [lb, max] on ballot counts (one compare per register and scalar
+// popcounts per probe); the keys at or above T are compacted into cand, and
+// each finds its place by counting the larger ones, one wave-uniform key
+// at a time.  Ties cannot occur, so the places are a permutation.  For
+// k <= 4 the argmax rounds cost less.
 // ---------------------------------------------------------------------------
 template <int PER_LANE>
-__device__ __forceinline__ int wave_select_topk(uint64_t *cand, int count, int k, uint64_t &kth) {
+__device__ __forceinline__ int wave_topk_keys(const uint64_t (&kv)[PER_LANE], int k, uint64_t lb,
+                                              uint64_t *cand, uint64_t &kth) {
+    if (k <= 4) return wave_rounds_topk<PER_LANE>(kv, k, cand, kth);
+    const int lane = lane_id();
+    const int count = count_ge(kv, 1);
+    const int nsel = count < k ? count : k;
+    const int cap = k <= 8 ? 16 : (k <= 16 ? 32 : 64);
+    uint64_t lo = 1;
+    int c_lo = count;
+    if (count > cap) {
+        if (lb > 1) {
+            const int c = count_ge(kv, lb);
+            if (c >= nsel) {
+                lo = lb;
+                c_lo = c;
+            }
+        }
+        if (c_lo > cap) {
+            uint64_t lm = kv[0];
+#pragma unroll
+            for (int i = 1; i < PER_LANE; ++i) lm = kv[i] > lm ? kv[i] : lm;
+            uint64_t hi = wave_max_u64(lm) + 1;   // no key reaches hi
+            // invariant: count_ge(lo) = c_lo > cap >= k > count_ge(hi)
+            while (c_lo > cap) {
+                const uint64_t mid = lo + ((hi - lo) >> 1);
+                const int c = count_ge(kv, mid);
+                if (c >= k) {
+                    lo = mid;
+                    c_lo = c;
+                } else {
+                    hi = mid;
+                }
+            }
+        }
+    }
+    // compact the keys >= lo (c_lo of them) into cand[0..c_lo)
+    const uint64_t lt = lanemask_lt();
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+        const bool p = kv[i] >= lo;
+        const uint64_t m = __ballot(p);
+        if (p) cand[base + popc64(m & lt)] = kv[i];
+        base += popc64(m);
+    }
+    wave_sync();
+    const uint64_t mine = lane < c_lo ? cand[lane] : 0;
+    wave_sync();
+    // place = number of larger keys (readlane returns int: widen unsigned)
+    const uint32_t mlo = uint32_t(mine), mhi = uint32_t(mine >> 32);
+    int place = 0;
+    for (int j = 0; j < c_lo; ++j) {
+        const uint64_t x = (uint64_t(uint32_t(__builtin_amdgcn_readlane(mhi, j))) << 32) |
+                           uint64_t(uint32_t(__builtin_amdgcn_readlane(mlo, j)));
+        place += x > mine ? 1 : 0;
+    }
+    if (lane < c_lo && place < nsel) cand[place] = mine;
+    const uint64_t km = __ballot(lane < c_lo && place == k - 1);
+    kth = 0;
+    if (km) {
+        const int l = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)km) - 1);
+        kth = (uint64_t(uint32_t(__builtin_amdgcn_readlane(mhi, l))) << 32) |
+              uint64_t(uint32_t(__builtin_amdgcn_readlane(mlo, l)));
+    }
+    wave_sync();
+    return nsel;
+}
+
+// The same for `count` keys in cand[0..count) (LDS, count <= 64 * PER_LANE).
+// ROUNDS: always the argmax rounds (the compactions inside the streaming
+// loop, where the search's code would crowd the loop's registers).
+template <int PER_LANE, bool ROUNDS = false>
+__device__ __forceinline__ int wave_select_topk(uint64_t *cand, int count, int k, uint64_t &kth,
+                                                uint64_t lb = 0) {
     const int lane = lane_id();
     uint64_t kv[PER_LANE];
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) {
-        int e = lane + kWave * i;
+        const int e = lane + kWave * i;
         kv[i] = e < count ? cand[e] : 0;
     }
     wave_sync();
-    const int nsel = count < k ? count : k;
-    uint64_t mine = 0;
-    for (int r = 0; r < nsel; ++r) {
-        uint64_t lm = kv[0];
-#pragma unroll
-        for (int i = 1; i < PER_LANE; ++i) lm = kv[i] > lm ? kv[i] : lm;
-        uint64_t wm = wave_max_u64(lm);
-#pragma unroll
-        for (int i = 0; i < PER_LANE; ++i) kv[i] = (kv[i] == wm) ? 0 : kv[i];
-        if (lane == r) mine = wm;
-    }
-    if (lane < nsel) cand[lane] = mine;
-    wave_sync();
-    uint64_t t = __shfl(mine, (k - 1) & 63, kWave);
-    kth = (nsel == k) ? t : 0;
-    return nsel;
+    if (ROUNDS) return wave_rounds_topk<PER_LANE>(kv, k, cand, kth);
+    return wave_topk_keys<PER_LANE>(kv, k, lb, cand, kth);
 }
 
 }  // namespace bastion
