@@ -1257,35 +1257,42 @@ __global__ __launch_bounds__(kThreads, (R >= 16 ? 2 : 4)) void build_trees_kerne
                          lane < nsel ? cand[lane] : uint64_t(0));
         }
         if (!arrive_last(P.row_ticket + row, uint32_t(P.S))) return;
-        // merge the S segment records of this row (wave 0)
+        // merge the S segment records of this row (wave 0); every load is
+        // issued before the first result is used (one round trip)
         if (wv == 0) {
             const char *base = P.partials + int64_t(row) * P.S * P.partial_bytes;
-            float lm = -INFINITY;
-            for (int s = lane; s < P.S; s += kWave)
-                lm = fmaxf(lm, ld_agent(reinterpret_cast<const float *>(base + int64_t(s) * P.partial_bytes)));
-            M = wave_max_f32(lm);
-            const float C = scale_ref(M);
-            float ls = 0.0f;
-            for (int s = lane; s < P.S; s += kWave) {
-                const float *r = reinterpret_cast<const float *>(base + int64_t(s) * P.partial_bytes);
-                ls += ld_agent(r + 1) * __builtin_amdgcn_exp2f(scale_ref(ld_agent(r)) - C);
-            }
-            Ssum = wave_sum_f32(ls);
-            uint64_t kth;
             const int tot = P.S * P.k;
             constexpr int kRegKeys = kCap / kWave;
-            if (tot <= kRegKeys * kWave) {
-                // every record's keys in registers, loaded at once; a record
-                // with k keys bounds the row's k-th best by its last one
-                uint64_t kv[kRegKeys], last = 0;
+            const bool in_regs = tot <= kRegKeys * kWave;
+            uint64_t kv[kRegKeys];
+#pragma unroll
+            for (int i = 0; i < kRegKeys; ++i) {
+                const int e = i * kWave + lane;
+                const int sg = e / P.k, j = e - sg * P.k;
+                kv[i] = in_regs && e < tot
+                            ? ld_agent(reinterpret_cast<const uint64_t *>(
+                                           base + int64_t(sg) * P.partial_bytes + 16) + j)
+                            : uint64_t(0);
+            }
+            // (m, s) of segment `lane` (S <= 64)
+            const uint64_t ms = lane < P.S ? ld_agent(reinterpret_cast<const uint64_t *>(
+                                                 base + int64_t(lane) * P.partial_bytes))
+                                           : uint64_t(0);
+            const float lm = lane < P.S ? __uint_as_float(uint32_t(ms)) : -INFINITY;
+            M = wave_max_f32(lm);
+            const float C = scale_ref(M);
+            const float ls = lane < P.S ? __uint_as_float(uint32_t(ms >> 32)) *
+                                              __builtin_amdgcn_exp2f(scale_ref(lm) - C)
+                                        : 0.0f;
+            Ssum = wave_sum_f32(ls);
+            uint64_t kth;
+            if (in_regs) {
+                // a record with k keys bounds the row's k-th best by its last one
+                uint64_t last = 0;
 #pragma unroll
                 for (int i = 0; i < kRegKeys; ++i) {
                     const int e = i * kWave + lane;
-                    const int sg = e / P.k, j = e - sg * P.k;
-                    kv[i] = e < tot ? ld_agent(reinterpret_cast<const uint64_t *>(
-                                                   base + int64_t(sg) * P.partial_bytes + 16) + j)
-                                    : uint64_t(0);
-                    if (e < tot && j == P.k - 1 && kv[i] > last) last = kv[i];
+                    if (e < tot && e % P.k == P.k - 1 && kv[i] > last) last = kv[i];
                 }
                 nsel = wave_topk_keys<kRegKeys>(kv, P.k, wave_max_u64(last), cand, kth);
             } else {

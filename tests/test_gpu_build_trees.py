@@ -30,7 +30,7 @@ def test_tiny_workload_full_parity():
     assert np.allclose(gc.np_(g["ahat"]), own["ahat"], rtol=1e-5)
 
 
-@pytest.mark.parametrize("segments", ["1", "3", "17"])
+@pytest.mark.parametrize("segments", ["1", "3", "17", "64"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_ragged_multi_segment(segments, dtype):
     binding.set_tuning(segments=int(segments))
