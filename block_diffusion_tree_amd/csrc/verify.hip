@@ -189,12 +189,20 @@ __global__ __launch_bounds__(256) void append_kernel(AttnArgs A) {
 }
 
 // ---- 2. attention ---------------------------------------------------------
-__device__ __forceinline__ float xor16_max(float v) {
-    return fmaxf(v, __shfl_xor(v, 16));
+// max over the four lanes r16 + 16 g4 of a row (lanes 16 and 32 apart),
+// with the cross-row swaps (VALU, no LDS round trip)
+__device__ __forceinline__ float row4_max(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // One 32-key step's tiles in LDS, shared by the block's waves: K as
-// [key][dim] (rows padded by 16 bytes), V as [dim][key] (rows padded by 16
+// [key][dim] (rows padded by 16 bytes; keys 8a + 4h + r of the step in row
+// 16h + 4a + r), V as [dim][key] (rows padded by 16
 // bytes); double-buffered.
 constexpr int kKPad = kD + 8, kVPad = kKeyStep + 8;
 
@@ -232,7 +240,11 @@ struct Steps {
             bf16x8 val = r[j][v];
             const int x = 64 * (q & 7) + lane;
             if (q < 8) {
-                *reinterpret_cast<bf16x8 *>(&ks[x >> 4][8 * (x & 15)]) = val;
+                // key 8a + 4h + r of the step goes to row 16h + 4a + r, so that
+                // S^T's two 16-row blocks give lane g4 the keys 8 g4 .. 8 g4 + 7
+                const int kp = q & 7;   // the piece's keys are 4 kp .. 4 kp + 3
+                const int row = 16 * (kp & 1) + 4 * (kp >> 1) + (lane >> 4);
+                *reinterpret_cast<bf16x8 *>(&ks[row][8 * (x & 15)]) = val;
             } else {
                 const int k8 = 8 * (x & 3);
                 if (!full) {
@@ -350,22 +362,23 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(AttnArgs A) {
                 s1[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qv[u][st], s1[u], 0, 0, 0);
             }
         }
-        // lane (r16, g4) now holds row r16's scores of keys kb + 4 g4 + r
-        // (s0) and kb + 16 + 4 g4 + r (s1), r = 0..3
+        // lane (r16, g4) now holds row r16's scores of keys kb + 8 g4 + r
+        // (s0) and kb + 8 g4 + 4 + r (s1), r = 0..3
         bf16x8 pb[kTpw];
 #pragma unroll
         for (int u = 0; u < kTpw; ++u) {
             if (!active[u]) continue;
             float v[8];
-            const int kq = kb + 4 * g4;
+            const int kq = kb + 8 * g4;
             const uint32_t *mrow = smask + ((w + kWaves * u) * kTile + r16) * A.W;
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                const float sc = (r < 4 ? s0[u][r] : s1[u][r - 4]) * A.scale_log2;
+                // raw score: the scale enters the max (monotone) and the exp2's fma
+                const float sc = r < 4 ? s0[u][r] : s1[u][r - 4];
                 if (plain) {
                     v[r] = sc;
                 } else {
-                    const int kk = kq + (r < 4 ? r : 12 + r);
+                    const int kk = kq + r;
                     const int j = min(max(kk - ctx, 0), A.T - 1);
                     const bool bit = (mrow[j >> 5] >> (j & 31)) & 1u;
                     const bool vis = kk < k1 && (kk < ctx || bit);
@@ -375,8 +388,7 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(AttnArgs A) {
             float tmax = v[0];
 #pragma unroll
             for (int r = 1; r < 8; ++r) tmax = fmaxf(tmax, v[r]);
-            tmax = xor16_max(tmax);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            tmax = row4_max(tmax) * A.scale_log2;
             // raise the reference of rows whose scores pass it by 2^kLazy
             const bool raise = tmax > m[u] + kLazy;
             if (__ballot(raise)) {   // wave-uniform, rare after the first steps
@@ -393,25 +405,18 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(AttnArgs A) {
             float ps = 0.0f;
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                const float p = live ? __builtin_amdgcn_exp2f(v[r] - m[u]) : 0.0f;
+                const float p =
+                    live ? __builtin_amdgcn_exp2f(__builtin_fmaf(v[r], A.scale_log2, -m[u])) : 0.0f;
                 ps += p;
                 pb[u][r] = __bf16(p);
             }
             lsum[u] += ps;
         }
-        // O^T += V^T P^T: V^T fragment j (dim 16 j + r16, keys in the order
-        // of the lane's scores, 4 of each S^T tile) read once for all tiles
+        // O^T += V^T P^T: V^T fragment j (dim 16 j + r16, the lane's keys
+        // 8 g4 .. 8 g4 + 7) read once for all tiles
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const __bf16 *vr = &vs[buf][16 * j + r16][4 * g4];
-            const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(vr);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(vr + 16);
-            bf16x8 av;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                av[r] = lo[r];
-                av[4 + r] = hi[r];
-            }
+            const bf16x8 av = *reinterpret_cast<const bf16x8 *>(&vs[buf][16 * j + r16][8 * g4]);
 #pragma unroll
             for (int u = 0; u < kTpw; ++u) {
                 if (!active[u]) continue;
