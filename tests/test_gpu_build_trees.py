@@ -124,6 +124,25 @@ def test_online_stop_around_the_first_stage(launch):
     assert gc.np_(g["n_nodes"]).tolist() == want
 
 
+@pytest.mark.parametrize("nmin", [2, 31, 32, 33])
+def test_online_stop_with_a_floor_near_the_first_stage(nmin):
+    """The same stepped cost tables with nmin around the 32-node first stage
+    of the trees' own launch, one table shared by every query in a second
+    call: stops below nmin move up to the first allowed peak."""
+    binding.set_tuning(split_trees=1)
+    wl = synth.scaled(synth.WORKLOADS["main"], B=8, V=32000, nmax=256, seed=1012)
+    x = gc.device_logits(wl)
+    cost = np.ones((wl.B, wl.nmax + 1))
+    for r, m in enumerate([1, 16, 30, 31, 32, 33, 60, None]):
+        if m is not None:
+            cost[r, m + 1:] = 1.0e6
+    cost[::2, 2:] += 1.0e-3   # a small step after one node on every other query
+    g, _ = gc.run_and_check(x, wl.k, wl.nmax, nmin=nmin, cost=torch.from_numpy(cost).to("cuda"))
+    assert (gc.np_(g["n_nodes"]) >= min(nmin, wl.nmax)).all()
+    shared = torch.from_numpy(cost[3]).to("cuda")
+    gc.run_and_check(x, wl.k, wl.nmax, nmin=nmin, cost=shared)
+
+
 def test_trees_in_their_own_launch():
     """Stream grids larger than the machine (here 1280 rows) build the trees
     in a launch of their own, with the online budget stop."""
