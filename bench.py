@@ -29,6 +29,8 @@ import time
 WORKLOAD_TEXT = {
     "main": "B=64 queries x b=16 positions x V=151936 bf16 logits, k=8, fixed N=64",
     "sweep": "B=256 x b=16 x V=128256 fp32 logits, k=4, online stop over N<=256",
+    "sweep_peaks": "B=256 x b=16 x V=128256 fp32 logits with the main workload's peaked rows "
+                   "(row max + U(2,10)), k=4, online stop over N<=256",
     "latency": "B=1 x b=16 x V=151936 bf16 logits, k=16, online stop over N<=128",
     "tiny": "B=1 x b=4 x V=1024 fp32 logits, k=4, fixed N=32",
     "mixture": "B=128 queries x K=8 branches x b=16 x V=151936 bf16 logits, k=8, mixture tree N=64",

@@ -459,10 +459,12 @@ struct TreeLayout {
     int pkey, ppar, prho, plrank, ppop, hist, plvl, q0col, fwork, total;
 };
 
-__host__ __device__ inline TreeLayout tree_layout(int b, int k, int nmax, int threads = kThreads) {
+// wide: the pool capacity of the trees' own launch (pool_cap_wide)
+__host__ __device__ inline TreeLayout tree_layout(int b, int k, int nmax, int threads = kThreads,
+                                                  bool wide = false) {
     TreeLayout L;
     const int nn = nmax + 2;
-    const int cap = pool_cap(tree_regs(nmax));
+    const int cap = wide ? pool_cap_wide(tree_regs(nmax)) : pool_cap(tree_regs(nmax));
     int o = 0;
     L.qtab = o; o = align16(o + 4 * b * qrow_stride(k));
     L.ttab = o; o = align16(o + 4 * b * qrow_stride(k));
@@ -663,11 +665,13 @@ __device__ void emit_tree(const BuildParams &P, int q, const int32_t *par, const
 }
 
 // st: this block's timestamps (stamped build), or null
-template <int G, int NT = kThreads, bool STAGED = false>
+// STAGED: the staged online build; WIDE: the larger pool (both in the trees'
+// own launch)
+template <int G, int NT = kThreads, bool STAGED = false, bool WIDE = false>
 __device__ __forceinline__ void tree_stage(const BuildParams &P, int q, char *smem, uint64_t *st) {
     (void)st;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const TreeLayout TL = tree_layout(P.b, P.k, P.nmax, NT);
+    const TreeLayout TL = tree_layout(P.b, P.k, P.nmax, NT, WIDE);
     RoundsLds S;
     S.qtab = reinterpret_cast<float *>(smem + TL.qtab);
     S.ttab = reinterpret_cast<int32_t *>(smem + TL.ttab);
@@ -686,7 +690,7 @@ __device__ __forceinline__ void tree_stage(const BuildParams &P, int q, char *sm
     const int64_t tk0 = int64_t(q) * bk;
     const int kp = qrow_stride(k);
     S.kp = kp;
-    constexpr int kPoolCap = pool_cap(G);
+    constexpr int kPoolCap = WIDE ? pool_cap_wide(G) : pool_cap(G);
     // per-depth columns for the family walks (FamilyCols)
     float *fq0 = reinterpret_cast<float *>(smem + TL.q0col);
     float *fq1n = fq0 + kColLen;
@@ -823,12 +827,23 @@ __device__ __forceinline__ void tree_stage(const BuildParams &P, int q, char *sm
                 FG.gpre = FW.gpre;
                 cnt = family_rank<NT>(PL, FG, nf, N, kPoolCap, S.par, S.dep, S.tok, S.rho, st);
             } else if (nf == -1) {
+                // one wave while the levels fit it, then the whole block
+                __shared__ int s_pw[3];
                 if (wv == 0) {
-                    const int n = pool_enumerate(PL, S.qtab, S.ttab, b, k, kp, t, kPoolCap);
-                    if (lane == 0) s_pool = n;
+                    PoolWide pw;
+                    const int n = pool_enumerate(PL, S.qtab, S.ttab, b, k, kp, t, kPoolCap, pw);
+                    if (lane == 0) {
+                        s_pool = n;
+                        s_pw[0] = pw.lo;
+                        s_pw[1] = pw.hi;
+                        s_pw[2] = pw.wide ? pw.d : 0;
+                    }
                 }
                 __syncthreads();
-                const int n = s_pool;
+                int n = s_pool;
+                if (n >= 1 && s_pw[2] > 0)
+                    n = pool_wide<NT>(PL, S.qtab, S.ttab, b, k, kp, t, kPoolCap, s_pw[0], s_pw[1],
+                                      s_pw[2], n);
                 if (n >= 1) cnt = pool_rank<NT>(PL, n, N, S.par, S.dep, S.tok, S.rho);
             }
             __syncthreads();
@@ -1534,7 +1549,7 @@ __global__ __launch_bounds__(tree_threads<R>()) void tree_kernel(BuildParams P) 
     extern __shared__ __align__(16) char smem[];
     uint64_t *st = P.stamps ? P.stamps + P.stamp_second * kStampSlots : nullptr;
     BASTION_STAMP(st, 3);
-    tree_stage<R, tree_threads<R>(), true>(P, int(blockIdx.x), smem, st);
+    tree_stage<R, tree_threads<R>(), true, true>(P, int(blockIdx.x), smem, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -1546,7 +1561,7 @@ static hipError_t launch_one(const BuildParams &P, int smem, hipStream_t s) {
     const int64_t grid = int64_t(P.B) * P.rows_per_query * P.S;
     hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), smem, s, P);
     if (MODE == 0 && P.split_trees) {
-        const int tsm = tree_layout(P.b, P.k, P.nmax, tree_threads<R>()).total;
+        const int tsm = tree_layout(P.b, P.k, P.nmax, tree_threads<R>(), true).total;
         if (tsm > 65536) {
             const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void *>(tree_kernel<R>),
                                                       hipFuncAttributeMaxDynamicSharedMemorySize, tsm);

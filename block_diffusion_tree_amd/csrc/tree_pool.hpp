@@ -41,6 +41,10 @@ constexpr int kMaxDigits = 10;      // levels of at most 1024 nodes (k >= 2)
 // pool slots for a tree of tree_regs(nmax) = G registers of 64 nodes: twice
 // the tree; none beyond G = 8 (the slot must fit the 10-bit key field)
 __host__ __device__ constexpr int pool_cap(int G) { return G <= 8 ? 128 * G : 0; }
+// the trees' own launch, with LDS to spare: four slots per tree node up to
+// G = 4 (1024 slots, what the field holds), so that loose bounds of deep
+// trees stay on the pool path
+__host__ __device__ constexpr int pool_cap_wide(int G) { return G <= 4 ? 256 * G : pool_cap(G); }
 constexpr int kLvlFloats = kFamilyLevels;   // family scratch
 
 typedef uint32_t pool_u32x4 __attribute__((ext_vector_type(4)));
@@ -95,10 +99,19 @@ __device__ __forceinline__ void rank_level(const PoolLds &L, int n0, int n) {
     }
 }
 
-// Step 2, by one wave: every node with rho >= t, parents before children.
-// Returns the node count, or -1 past cap.
+// Where the one-wave enumeration stops: the first level wider than a wave
+// (its nodes [lo, hi) ranked, d the next depth); the block continues there
+// (pool_wide).
+struct PoolWide {
+    int lo, hi, d;
+    bool wide;
+};
+
+// Step 2, by one wave: every node with rho >= t, parents before children,
+// up to the first level wider than a wave (then w.wide is set and the block
+// goes on with pool_wide).  Returns the node count so far, or -1 past cap.
 __device__ int pool_enumerate(const PoolLds &L, const float *qtab, const int32_t *ttab, int b,
-                              int k, int kp, float t, int cap) {
+                              int k, int kp, float t, int cap, PoolWide &w) {
     const int lane = lane_id();
     const uint64_t lt = lanemask_lt();
     // lane l < 32 holds q of rank 0 at depth l+1, lane 32 + l that of rank 1;
@@ -212,13 +225,31 @@ __device__ int pool_enumerate(const PoolLds &L, const float *qtab, const int32_t
             lr = alive ? L.lrank[slot] : 0;
         }
     }
-    if (over) return -1;
-    if (!wide) return n;
-    // levels wider than a wave: lane l handles rank l % kk of parent l / kk
-    // of a chunk (kk: k rounded up to a power of two)
+    w.lo = lo;
+    w.hi = hi;
+    w.d = d;
+    w.wide = wide;
+    return over ? -1 : n;
+}
+
+// Step 2 continued, by the whole block, from the first wide level: each
+// thread takes rank j (of k rounded up to a power of two) of one parent;
+// the level's qualifying children get slots through a block-wide prefix of
+// the waves' ballots, then every thread ranks some of them inside the level
+// (slot order within a level is free: the in-level rank orders the keys).
+// Returns the node count, or -1 past cap (block-uniform).  Ends with a
+// barrier.
+template <int THREADS>
+__device__ int pool_wide(const PoolLds &L, const float *qtab, const int32_t *ttab, int b, int k,
+                         int kp, float t, int cap, int lo, int hi, int d, int n) {
+    constexpr int W = THREADS / kWave;
+    __shared__ int s_cnt[W];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const uint64_t lt = lanemask_lt();
     int sh = 0;
     while ((1 << sh) < k) ++sh;
-    const int pl = lane >> sh, j = lane & ((1 << sh) - 1), ppc = kWave >> sh;
+    const int pl = tid >> sh, j = tid & ((1 << sh) - 1), ppc = THREADS >> sh;
     const int jc = j < k ? j : k - 1;
     for (; d <= b && hi > lo; ++d) {
         const int np = hi - lo;
@@ -233,20 +264,28 @@ __device__ int pool_enumerate(const PoolLds &L, const float *qtab, const int32_t
             const int pr = L.lrank[pc];
             const bool ok = valid && v >= t;
             const uint64_t m = __ballot(ok);
-            const int c = __builtin_amdgcn_readfirstlane(popc64(m));
-            if (n + c > cap) return -1;
+            if (lane == 0) s_cnt[wv] = popc64(m);
+            __syncthreads();
+            int before = 0, tot = 0;
+#pragma unroll
+            for (int x = 0; x < W; ++x) {
+                const int c = s_cnt[x];
+                before += x < wv ? c : 0;
+                tot += c;
+            }
+            if (n + tot > cap) return -1;
             if (ok) {
-                const int s = n + popc64(m & lt);
+                const int s = n + before + popc64(m & lt);
                 L.key[s] = tree_key(v, d, tj, pr);
                 L.par[s] = pc;
                 L.rho[s] = v;
             }
-            n = __builtin_amdgcn_readfirstlane(n + c);
+            n += tot;
+            __syncthreads();   // the counts are read; the level's keys are written
         }
-        wave_sync();
-        rank_level(L, n0, n);
-        wave_sync();
-        lo = hi;
+        for (int s = n0 + tid; s < n; s += THREADS) L.lrank[s] = count_greater(L.key, n0, n, L.key[s]);
+        __syncthreads();
+        lo = n0;
         hi = n;
     }
     return n;

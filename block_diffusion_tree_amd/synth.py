@@ -63,6 +63,10 @@ WORKLOADS = {
                      "rowmax_peak", 2.0, 10.0),
     # budget-controller sweep over a Llama-3.1-sized vocabulary, fp32.
     "sweep": Workload("sweep", 256, 16, 128256, F32, 4, 256, 1, True, 1003, "gauss_bump"),
+    # the sweep's shape and budget with the main workload's peaked rows, where
+    # N* lands deep in the budget (a labelled extra sweep).
+    "sweep_peaks": Workload("sweep_peaks", 256, 16, 128256, F32, 4, 256, 1, True, 1013,
+                            "rowmax_peak", 2.0, 10.0),
     # single query latency case with confident rows.
     "latency": Workload("latency", 1, 16, 151936, BF16, 16, 128, 1, True, 1004,
                         "rowmax_peak", 6.0, 12.0),

@@ -156,12 +156,14 @@ def test_trees_in_their_own_launch():
         assert torch.equal(g[f], g2[f]), f
 
 
-def test_sweep_full_workload_full_parity():
+@pytest.mark.parametrize("name", ["sweep", "sweep_peaks"])
+def test_sweep_full_workload_full_parity(name):
     """The whole budget-sweep workload in one call, as the benchmark launches
     it (4096 rows, trees in their own launch, online stop): every row against
     the reference's float64 softmax and top-k; every tree, mask and position
-    against the reference fed the GPU's own q."""
-    wl = synth.WORKLOADS["sweep"]
+    against the reference fed the GPU's own q.  sweep_peaks: the same shape
+    with peaked rows, whose stops fall deep in the budget."""
+    wl = synth.WORKLOADS[name]
     x = synth.make_logits(wl, device="cuda")
     cost = cost_table(wl.B, wl.nmax, wl.seed, synth.LATENCY_A100)
     g = binding.build_trees(x, k=wl.k, nmax=wl.nmax, nmin=1, cost=cost, l_ar=1.0)
