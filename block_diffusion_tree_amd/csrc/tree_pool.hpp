@@ -58,6 +58,7 @@ struct PoolLds {
     int32_t *lrank;    // [cap] rank inside its level
     int32_t *pop;      // [cap] pop index
     uint32_t *hist;    // [kHistBins]
+    uint64_t *sbuf;    // [cap] sort scratch (trees' own launch), or null
 };
 
 
@@ -97,6 +98,70 @@ __device__ __forceinline__ void rank_level(const PoolLds &L, int n0, int n) {
         const int r = count_greater(L.key, n0, n, x);
         if (s < n) L.lrank[s] = r;
     }
+}
+
+// Large pools and levels are ranked by sorting instead of counting every
+// pair: a bitonic sort of the keys over the whole block (partners inside a
+// wave through DPP / permlane swaps, across waves through LDS), then each
+// key's place by binary search in the sorted copy.  Used past kSortMin keys
+// when the block holds the next power of two.
+constexpr int kSortMin = 512;
+
+// sbuf[0, M) = keys[0, m) in descending order, zeros after (M: the power of
+// two >= max(m, 64), at most THREADS; sbuf apart from keys).  Whole block;
+// ends with a barrier.
+template <int THREADS>
+__device__ void block_sort_desc(uint64_t *sbuf, const uint64_t *keys, int m) {
+    const int tid = threadIdx.x;
+    int M = kWave;
+    while (M < m) M <<= 1;
+    const bool act = tid < M;
+    const uint64_t x0 = tid < m ? keys[tid] : uint64_t(0);
+    uint32_t h = uint32_t(x0 >> 32), l = uint32_t(x0);
+    for (int k = 2; k <= M; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const bool desc = (tid & k) == 0;
+            if (j >= kWave) {
+                if (act) sbuf[tid] = (uint64_t(h) << 32) | l;
+                __syncthreads();
+                if (act) {
+                    const uint64_t o = sbuf[tid ^ j];
+                    const uint32_t oh = uint32_t(o >> 32), ol = uint32_t(o);
+                    const bool ogt = key_gt(oh, ol, h, l);
+                    const bool lower = (tid & j) == 0;
+                    const bool take = (desc == lower) ? ogt : !ogt;
+                    h = take ? oh : h;
+                    l = take ? ol : l;
+                }
+                __syncthreads();
+            } else if (j == 32) {
+                cmpx<32>(h, l, desc);
+            } else if (j == 16) {
+                cmpx<16>(h, l, desc);
+            } else if (j == 8) {
+                cmpx<8>(h, l, desc);
+            } else if (j == 4) {
+                cmpx<4>(h, l, desc);
+            } else if (j == 2) {
+                cmpx<2>(h, l, desc);
+            } else {
+                cmpx<1>(h, l, desc);
+            }
+        }
+    }
+    if (act) sbuf[tid] = (uint64_t(h) << 32) | l;
+    __syncthreads();
+}
+
+// number of keys above x in sbuf[0, m), sorted descending
+__device__ __forceinline__ int sorted_above(const uint64_t *sbuf, int m, uint64_t x) {
+    int lo = 0, hi = m;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (sbuf[mid] > x) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
 }
 
 // Where the one-wave enumeration stops: the first level wider than a wave
@@ -283,7 +348,16 @@ __device__ int pool_wide(const PoolLds &L, const float *qtab, const int32_t *tta
             n += tot;
             __syncthreads();   // the counts are read; the level's keys are written
         }
-        for (int s = n0 + tid; s < n; s += THREADS) L.lrank[s] = count_greater(L.key, n0, n, L.key[s]);
+        const int m = n - n0;
+        int mp = kWave;
+        while (mp < m) mp <<= 1;
+        if (L.sbuf && m > kSortMin && mp <= THREADS) {
+            block_sort_desc<THREADS>(L.sbuf, L.key + n0, m);
+            for (int s = n0 + tid; s < n; s += THREADS) L.lrank[s] = sorted_above(L.sbuf, m, L.key[s]);
+        } else {
+            for (int s = n0 + tid; s < n; s += THREADS)
+                L.lrank[s] = count_greater(L.key, n0, n, L.key[s]);
+        }
         __syncthreads();
         lo = n0;
         hi = n;
@@ -301,18 +375,25 @@ __device__ __forceinline__ int pool_rank(const PoolLds &L, int n, int nmax, int3
                                          int32_t *dep, int32_t *tok, float *rho) {
     constexpr int W = THREADS / kWave;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-    const int groups = (n + kWave - 1) / kWave;
-    const int split = groups >= W ? 1 : W / groups;   // waves per group
-    const int chunk = (n + split - 1) / split;
-    for (int e = tid; e < n; e += THREADS) L.pop[e] = 1;
-    __syncthreads();
-    for (int g0 = wv / split; g0 < groups; g0 += W / split) {
-        const int e = g0 * kWave + lane;
-        const int part = wv % split;
-        const int f0 = part * chunk, f1 = f0 + chunk < n ? f0 + chunk : n;
-        if (e < n) {
-            const int r = count_greater(L.key, f0, f1, L.key[e]);
-            if (r) atomicAdd(L.pop + e, r);
+    int np2 = kWave;
+    while (np2 < n) np2 <<= 1;
+    if (L.sbuf && n > kSortMin && np2 <= THREADS) {
+        block_sort_desc<THREADS>(L.sbuf, L.key, n);
+        for (int e = tid; e < n; e += THREADS) L.pop[e] = 1 + sorted_above(L.sbuf, n, L.key[e]);
+    } else {
+        const int groups = (n + kWave - 1) / kWave;
+        const int split = groups >= W ? 1 : W / groups;   // waves per group
+        const int chunk = (n + split - 1) / split;
+        for (int e = tid; e < n; e += THREADS) L.pop[e] = 1;
+        __syncthreads();
+        for (int g0 = wv / split; g0 < groups; g0 += W / split) {
+            const int e = g0 * kWave + lane;
+            const int part = wv % split;
+            const int f0 = part * chunk, f1 = f0 + chunk < n ? f0 + chunk : n;
+            if (e < n) {
+                const int r = count_greater(L.key, f0, f1, L.key[e]);
+                if (r) atomicAdd(L.pop + e, r);
+            }
         }
     }
     __syncthreads();
