@@ -11,20 +11,20 @@
 //      node one deviation away from it.  The family's rho values go into a
 //      1024-bin histogram of their float bits; t is the lower edge of the
 //      first bin (from the top) where the count reaches N.
-//   2. one wave enumerates, level by level, every node with rho >= t.  A
-//      parent's children come in rank order with non-increasing rho (q is
-//      sorted and float products are monotone), so each parent contributes
-//      a prefix of its ranks.  Such pools are a few parallel chains that
-//      branch at uncertain positions: each lane carries one chain in
-//      registers.  A node's key holds its parent's rank inside the parent's
-//      level, which is best-first's order for children of different parents
-//      that agree on (rho, depth, token); keys are then unique and compare
-//      exactly as best-first pops.  On a level where no chain branches, each
-//      child keeps its parent's in-level rank (same token, monotone rho, and
-//      the chains that stop are the last ones), so only branching levels
-//      rank their nodes, through LDS.  Levels wider than a wave are expanded
-//      from LDS.  The caller falls back to the exact round-by-round build if
-//      the pool outgrows its capacity.
+//   2. every node with rho >= t, level by level.  A parent's children come
+//      in rank order with non-increasing rho (q is sorted and float products
+//      are monotone), so each parent contributes a prefix of its ranks.
+//      Such pools are a few parallel chains that branch at uncertain
+//      positions: one wave follows them, a chain per lane in registers,
+//      while none branches (each child keeps its parent's in-level rank:
+//      same token, monotone rho, and the chains that stop are the last
+//      ones); from the first level where one branches the whole block
+//      expands the levels from LDS and ranks each one.  A node's key holds
+//      its parent's rank inside the parent's level, which is best-first's
+//      order for children of different parents that agree on (rho, depth,
+//      token); keys are then unique and compare exactly as best-first pops.
+//      The caller falls back to the exact round-by-round build if the pool
+//      outgrows its capacity.
 //   3. the block counts, for every pool node, the larger keys; the count is
 //      its pop index minus one, and the first min(pool, N) are the tree.
 #pragma once
@@ -87,17 +87,6 @@ __device__ __forceinline__ int count_greater(const uint64_t *keys, int f0, int f
         for (int i = 0; i < 8; ++i) r += (f + i < f1 && y[i] > x) ? 1 : 0;
     }
     return r;
-}
-
-// in-level ranks of slots [n0, n) (one wave)
-__device__ __forceinline__ void rank_level(const PoolLds &L, int n0, int n) {
-    const int lane = lane_id();
-    for (int s0 = n0; s0 < n; s0 += kWave) {
-        const int s = s0 + lane;
-        const uint64_t x = s < n ? L.key[s] : ~uint64_t(0);
-        const int r = count_greater(L.key, n0, n, x);
-        if (s < n) L.lrank[s] = r;
-    }
 }
 
 // Large pools and levels are ranked by sorting instead of counting every
@@ -164,17 +153,18 @@ __device__ __forceinline__ int sorted_above(const uint64_t *sbuf, int m, uint64_
     return lo;
 }
 
-// Where the one-wave enumeration stops: the first level wider than a wave
-// (its nodes [lo, hi) ranked, d the next depth); the block continues there
-// (pool_wide).
+// Where the one-wave enumeration stops: the first level where a chain
+// branches (its parents [lo, hi), ranked inside their level, d its depth);
+// the block continues there (pool_wide).
 struct PoolWide {
     int lo, hi, d;
     bool wide;
 };
 
 // Step 2, by one wave: every node with rho >= t, parents before children,
-// up to the first level wider than a wave (then w.wide is set and the block
-// goes on with pool_wide).  Returns the node count so far, or -1 past cap.
+// up to the first level where a chain branches (then w.wide is set and the
+// block goes on with pool_wide).  Returns the node count so far, or -1 past
+// cap.
 __device__ int pool_enumerate(const PoolLds &L, const float *qtab, const int32_t *ttab, int b,
                               int k, int kp, float t, int cap, PoolWide &w) {
     const int lane = lane_id();
@@ -233,61 +223,9 @@ __device__ int pool_enumerate(const PoolLds &L, const float *qtab, const int32_t
             n = __builtin_amdgcn_readfirstlane(n + c);
             hi = n;
         } else {
-            // every child of the level, rank by rank; then rank the level
-            // and hand its nodes to the lanes
-            const int n0 = n;
-            for (int j0 = 0; j0 < k; j0 += 8) {
-                // eight ranks at a time, loaded together (zero padding past k)
-                const pool_f32x4 *q4 = reinterpret_cast<const pool_f32x4 *>(qtab + (d - 1) * kp + j0);
-                const pool_i32x4 *t4 = reinterpret_cast<const pool_i32x4 *>(ttab + (d - 1) * kp + j0);
-                const pool_f32x4 qa = q4[0], qb = q4[1];
-                const pool_i32x4 ta = t4[0], tb = t4[1];
-                const float qv[8] = {qa[0], qa[1], qa[2], qa[3], qb[0], qb[1], qb[2], qb[3]};
-                const int tv[8] = {ta[0], ta[1], ta[2], ta[3], tb[0], tb[1], tb[2], tb[3]};
-                float v[8];
-                uint64_t m[8];
-                int c[8], tot = 0;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    v[i] = __fmul_rn(rho, qv[i]);
-                    m[i] = __ballot(alive && j0 + i < k && v[i] >= t);
-                    c[i] = popc64(m[i]);
-                    tot += c[i];
-                }
-                tot = __builtin_amdgcn_readfirstlane(tot);
-                if (n + tot > cap) {
-                    over = true;
-                    break;
-                }
-                int base = n;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    if ((m[i] >> lane) & 1u) {
-                        const int s = base + popc64(m[i] & lt);
-                        L.key[s] = tree_key(v[i], d, tv[i], lr);
-                        L.par[s] = slot;
-                        L.rho[s] = v[i];
-                    }
-                    base += c[i];
-                }
-                n = __builtin_amdgcn_readfirstlane(n + tot);
-                if (m[7] == 0) break;   // later ranks give no larger rho
-            }
-            if (over) break;
-            wave_sync();
-            rank_level(L, n0, n);
-            wave_sync();
-            lo = n0;
-            hi = n;
-            if (hi - lo > kWave) {
-                wide = true;
-                ++d;
-                break;
-            }
-            alive = lane < hi - lo;
-            slot = lo + (alive ? lane : 0);
-            rho = alive ? L.rho[slot] : 0.0f;
-            lr = alive ? L.lrank[slot] : 0;
+            // a chain branches: the block takes over at this level
+            wide = true;
+            break;
         }
     }
     w.lo = lo;
@@ -297,7 +235,7 @@ __device__ int pool_enumerate(const PoolLds &L, const float *qtab, const int32_t
     return over ? -1 : n;
 }
 
-// Step 2 continued, by the whole block, from the first wide level: each
+// Step 2 continued, by the whole block, from the first branching level: each
 // thread takes rank j (of k rounded up to a power of two) of one parent;
 // the level's qualifying children get slots through a block-wide prefix of
 // the waves' ballots, then every thread ranks some of them inside the level
