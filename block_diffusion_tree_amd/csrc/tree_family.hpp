@@ -131,7 +131,9 @@ struct FamRegs {
 // Returns the lower bound t (every wave reads the histogram itself), 0 when
 // the family holds fewer than n nodes; with bound2, also the bound of n2
 // nodes.
-template <int THREADS>
+// TWO: also count the nodes of the paths that take rank 1 at two depths
+// (real nodes outside the family: they only tighten the bound)
+template <int THREADS, bool TWO = false>
 __device__ __forceinline__ float family_bound(const float *qtab, const int32_t *ttab,
                                               const FamilyCols &F, int b, int k, int kp, int n,
                                               uint32_t *hist, float *lvl, FamRegs &R,
@@ -212,6 +214,21 @@ __device__ __forceinline__ float family_bound(const float *qtab, const int32_t *
                         r = __fmul_rn(r, d == c.e ? c.qe : q4[u]);
                         if (d > D) atomicAdd(hist + (d >= lo ? hist_bin(r) : kHistBins + lane), 1u);
                     }
+                }
+            }
+        }
+    }
+    if (TWO && D < b && k > 1) {
+        // rank 1 at depths e1 < e2, rank 0 elsewhere: the nodes at depths
+        // >= e2 below the complete levels, with rho in best-first's order
+        for (int pi = tid; pi < b * b; pi += THREADS) {
+            const int e1 = pi / b + 1, e2 = pi - (e1 - 1) * b + 1;
+            if (e1 < e2) {
+                float r = 1.0f;
+                for (int d = 1; d <= b; ++d) {
+                    const float q = (d == e1 || d == e2) ? qtab[(d - 1) * kp + 1] : F.q0[d - 1];
+                    r = __fmul_rn(r, q);
+                    if (d >= e2 && d > D) atomicAdd(hist + hist_bin(r), 1u);
                 }
             }
         }
