@@ -12,11 +12,17 @@ rotating 5 GB batches.
 
 Prints one JSON line.  `value` is trees per second over the timed steps.
 `roofline` is the fused kernel's algorithmic bytes per launch (every logit
-read once plus every output written once) over its mean launch time,
-measured with HIP events recorded on the stream the kernel runs on (for the
-mixture call, the span of its two launches: the stream kernel and the
-per-query stage).
+read once plus every output written once) over its mean launch time: the
+span of HIP events recorded on the kernel's stream before and after the K
+back-to-back calls of the timed region, over K (a call of the mixture is its
+two launches: the stream kernel and the per-query stage).  Single-call
+times (mean, p10 / p50 / p90) come from a second pass with events around
+each call; those events add the command processor's gap between packets.
 `cpu_baseline` times the CPU reference on the same batch (host copy).
+`in_flight` is the rate with two batches in flight (consecutive calls on
+two streams, each with its own workspace and outputs): a call's last trees
+then overlap the next call's stream, which a serving loop with two
+independent batches gets; `value` stays the one-call-at-a-time rate.
 """
 from __future__ import annotations
 
@@ -58,7 +64,7 @@ def parse():
                          "(bastion_mixture_marginal, a second pass over the branch rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the warm-input, accept and streaming-ceiling timings "
+                    help="skip the warm-input, accept, streaming-ceiling and two-in-flight timings "
                          "(profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device-to-device copy of this many MiB "
@@ -199,7 +205,6 @@ def stream_ceiling(bufs, dev, reps=20):
     (libbastion_probe.so) over the same input buffers, rotating like the
     timed steps, for a few grid sizes; the best rate in GB/s and its grid."""
     import ctypes as C
-    import numpy as np
     import torch
     from block_diffusion_tree_amd import build as hipbuild
     if not os.path.exists(hipbuild.PROBE_LIB):
@@ -222,18 +227,32 @@ def stream_ceiling(bufs, dev, reps=20):
                 raise RuntimeError(f"stream probe failed ({st})")
         for i in range(3):
             go(i)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(reps)]
+        # timed like the steps: one pair of events around reps back-to-back launches
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
         for i in range(reps):
-            ev[i][0].record(stream)
             go(i)
-            ev[i][1].record(stream)
+        b.record(stream)
         torch.cuda.synchronize()
-        us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+        us = a.elapsed_time(b) * 1e3 / reps
         gbs = nbytes / (us * 1e-6) / 1e9
         if best is None or gbs > best["gbs"]:
             best = dict(gbs=gbs, us=us, blocks=blocks, bytes=nbytes)
     return best
+
+
+def time_span(fn, n, stream):
+    """One pair of HIP events around n back-to-back calls of fn(i) on
+    `stream`: the mean time per call in ms."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(n):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
 
 
 def time_launches(fn, n, stream):
@@ -331,12 +350,18 @@ def main_verify(args):
         call()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    launch_ms = time_launches(lambda i: call(), args.steps, stream)
+    e_start.record(stream)
+    for _ in range(args.steps):
+        call()
+    e_end.record(stream)
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    launch_ms = time_launches(lambda i: call(), args.steps, stream)
     nbytes, flops = verify_bytes_flops(vw, ctx_np)
-    mean_ms = float(launch_ms.mean())
+    mean_ms = e_start.elapsed_time(e_end) / args.steps
     achieved = nbytes / (mean_ms * 1e-3) / 1e9
     line = {
         "metric": "tree-attention layer: verified trees/sec + achieved HBM GB/s, S=64 T=65, 1 MI355X",
@@ -354,7 +379,11 @@ def main_verify(args):
                                "of one bastion_tree_attention call, timed together",
                      "alg_bytes_per_launch": nbytes,
                      "launch_us_mean": mean_ms * 1e3,
-                     "launch_us_p50": float(np.median(launch_ms)) * 1e3,
+                     "launch_timing": "events around the K back-to-back calls of the timed "
+                                      "region; single-call figures from a second pass with "
+                                      "events around each call",
+                     "single_call_us_mean": float(launch_ms.mean()) * 1e3,
+                     "single_call_us_p50": float(np.median(launch_ms)) * 1e3,
                      "mfma": {"flops_per_launch": flops,
                               "achieved_tflops": flops / (mean_ms * 1e-3) / 1e12,
                               "peak_tflops": 2500.0,
@@ -428,27 +457,33 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # the timed region: K calls back to back, one pair of HIP events on the
+    # stream around them (an event record between calls is a packet of its
+    # own for the command processor and would add its gap to every step)
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e_start.record(stream)
     for i in range(args.steps):
-        ev[i][0].record(stream)
         step(i)
-        ev[i][1].record(stream)
+    e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    span_ms = e_start.elapsed_time(e_end)
+    # the spread of single calls: a second pass with events around each call
+    launch_ms = time_launches(step, args.steps, stream)
 
     extras = {}
     if not args.no_extras:
         # warm: the same input batch every call (what the MALL keeps of it)
-        warm_ms = time_launches(lambda i: calls[0](), max(10, args.steps // 2), stream)
-        extras["warm"] = {"launch_us_mean": float(warm_ms.mean()) * 1e3,
-                          "launch_us_p50": float(np.median(warm_ms)) * 1e3,
-                          "launch_us_p10": float(np.percentile(warm_ms, 10)) * 1e3,
-                          "launch_us_p90": float(np.percentile(warm_ms, 90)) * 1e3}
+        nw = max(10, args.steps // 2)
+        warm_mean = time_span(lambda i: calls[0](), nw, stream)
+        warm_ms = time_launches(lambda i: calls[0](), nw, stream)
+        extras["warm"] = {"launch_us_mean": warm_mean * 1e3,
+                          "single_call_us_p50": float(np.median(warm_ms)) * 1e3,
+                          "single_call_us_p10": float(np.percentile(warm_ms, 10)) * 1e3,
+                          "single_call_us_p90": float(np.percentile(warm_ms, 90)) * 1e3}
         if not mixture:
             # bastion_accept on the trees of buffer 0, timed on its own
             o = outs[0]
@@ -464,6 +499,38 @@ def main():
                                 "launch_us_p50": float(np.median(acc_ms)) * 1e3,
                                 "mean_accept_len": float(alen.float().mean())}
         extras["ceiling"] = stream_ceiling(bufs, dev)
+        # two batches in flight: consecutive calls alternate between two
+        # streams, each with its own workspace and outputs, so that one
+        # call's tail (its last trees) overlaps the next call's stream
+        s2 = torch.cuda.Stream(device=dev)
+        ws2 = binding.Workspace(dev)
+        with torch.cuda.stream(s2):
+            if mixture:
+                mouts2 = [alloc(wl.B, wl.K, wl.b, wl.k, dev) for _ in range(nbuf)]
+                outs2 = [binding.alloc_tree_out(wl.B, wl.b, wl.k, wl.nmax, dev, with_rows=False)
+                         for _ in range(nbuf)]
+                calls2 = [prep(bufs[j], prior, k=wl.k, nmax=wl.nmax, out=mouts2[j], tree=outs2[j],
+                               ws=ws2)[2] for j in range(nbuf)]
+            else:
+                outs2 = [binding.alloc_tree_out(wl.B, wl.b, wl.k, wl.nmax, dev) for _ in range(nbuf)]
+                calls2 = [binding.prepare_build_trees(bufs[j], k=wl.k, nmax=wl.nmax, nmin=wl.nmin,
+                                                      cost=cost, out=outs2[j], ws=ws2)[1]
+                          for j in range(nbuf)]
+        pair = (calls, calls2)
+        for i in range(2 * nbuf):
+            pair[i % 2][i % nbuf]()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(args.steps):
+            pair[i % 2][i % nbuf]()
+        torch.cuda.synchronize()
+        fl_us = (time.perf_counter() - t1) * 1e6 / args.steps
+        # stream 2 ran on the odd buffers: its outputs must equal the serial ones
+        same = all(torch.equal(outs2[j][f], outs[j][f]) for j in range(1, nbuf, 2)
+                   for f in ("parent", "token", "rho", "n_nodes"))
+        extras["in_flight"] = {"batches": 2, "us_per_step": fl_us,
+                               "trees_per_s": wl.B / (fl_us * 1e-6),
+                               "outputs_match_serial": bool(same)}
 
     ms_per_step = wall * 1e3 / args.steps
     # the marginal rule reads every branch logit twice: its ranking needs
@@ -471,7 +538,7 @@ def main():
     alg_bytes = wl.logit_bytes * (2 if marginal else 1) + out_bytes(outs[0])
     if mixture:
         alg_bytes += out_bytes(mouts[0]) + prior.numel() * 4
-    mean_ms = float(launch_ms.mean())
+    mean_ms = span_ms / args.steps
     achieved = alg_bytes / (mean_ms * 1e-3) / 1e9
     traffic = None
     if os.path.exists(args.traffic_json):
@@ -503,9 +570,13 @@ def main():
                                 "in a launch of their own; the call's launches timed together"),
                      "alg_bytes_per_launch": alg_bytes,
                      "launch_us_mean": mean_ms * 1e3,
-                     "launch_us_p50": float(np.median(launch_ms)) * 1e3,
-                     "launch_us_p10": float(np.percentile(launch_ms, 10)) * 1e3,
-                     "launch_us_p90": float(np.percentile(launch_ms, 90)) * 1e3},
+                     "launch_timing": "events around the K back-to-back calls of the timed "
+                                      "region; the single-call figures below from a second "
+                                      "pass with events around each call",
+                     "single_call_us_mean": float(launch_ms.mean()) * 1e3,
+                     "single_call_us_p50": float(np.median(launch_ms)) * 1e3,
+                     "single_call_us_p10": float(np.percentile(launch_ms, 10)) * 1e3,
+                     "single_call_us_p90": float(np.percentile(launch_ms, 90)) * 1e3},
     }
     if mixture:
         # A_hat of the emitted trees (the rules' expected committed tokens)
@@ -530,6 +601,11 @@ def main():
         line["warm"] = w
     if "accept" in extras:
         line["accept"] = extras["accept"]
+    if "in_flight" in extras:
+        f = extras["in_flight"]
+        f["achieved_gbs"] = alg_bytes / (f["us_per_step"] * 1e-6) / 1e9
+        f["frac_of_peak"] = f["achieved_gbs"] / HBM_PEAK_GBS
+        line["in_flight"] = f
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev)
