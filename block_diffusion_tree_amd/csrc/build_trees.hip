@@ -829,7 +829,7 @@ __device__ __forceinline__ void tree_stage(const BuildParams &P, int q, char *sm
                 FG.ttab = S.ttab;
                 FG.cmask = FW.cmask;
                 FG.gpre = FW.gpre;
-                cnt = family_rank<NT>(PL, FG, nf, N, kPoolCap, S.par, S.dep, S.tok, S.rho, st);
+                cnt = family_rank<NT>(PL, FG, nf, N, t, S.par, S.dep, S.tok, S.rho, st);
             } else if (nf == -1) {
                 // one wave while the levels fit it, then the whole block
                 __shared__ int s_pw[3];
@@ -842,13 +842,16 @@ __device__ __forceinline__ void tree_stage(const BuildParams &P, int q, char *sm
                         s_pw[1] = pw.hi;
                         s_pw[2] = pw.wide ? pw.d : 0;
                     }
+                } else {
+                    // meanwhile the other waves clear pool_rank's bins
+                    for (int i = tid - kWave; i < kHistBins; i += NT - kWave) PL.hist[i] = 0u;
                 }
                 __syncthreads();
                 int n = s_pool;
                 if (n >= 1 && s_pw[2] > 0)
                     n = pool_wide<NT>(PL, S.qtab, S.ttab, b, k, kp, t, kPoolCap, s_pw[0], s_pw[1],
                                       s_pw[2], n);
-                if (n >= 1) cnt = pool_rank<NT>(PL, n, N, S.par, S.dep, S.tok, S.rho);
+                if (n >= 1) cnt = pool_rank<NT>(PL, n, N, t, S.par, S.dep, S.tok, S.rho);
             }
             __syncthreads();
         }

@@ -20,9 +20,11 @@
 //                  holds the whole pool.  Otherwise the caller enumerates the
 //                  pool level by level (tree_pool.hpp).
 //   family_rank:   a node's pop index is one plus the number of pool keys
-//                  that pop before it; equal (rho, depth, token) keys are
-//                  ordered as best-first orders them, by their parents, which
-//                  the nodes' family identities resolve directly.
+//                  that pop before it: every key of a higher rho bin, and
+//                  those of its own bin that compare above it; equal (rho,
+//                  depth, token) keys are ordered as best-first orders them,
+//                  by their parents, which the nodes' family identities
+//                  resolve directly.
 //
 // All three run branch-light on every wave of the block: one wave's
 // dependent LDS round trips and VALU-to-scalar transitions dominate here,
@@ -422,6 +424,8 @@ __device__ int family_select(const PoolLds &L, const float *qtab, const int32_t 
     }
     const int dummy = cap + kPoolPad + lane;
     if (tid < kPoolPad) L.key[n + tid] = 0;
+    // family_rank's bins (every wave has read the bound's histogram)
+    for (int i = tid; i < kHistBins; i += THREADS) L.hist[i] = 0u;
     const int baseB = nA;
     // the top-1 path's first family node (depth D + 1), for the parent links
     const int topbase = npair >= 0 ? baseB + Wk.flag[1] +
@@ -570,65 +574,26 @@ __device__ __forceinline__ int fam_parent(const FamGeom &G, uint64_t x, int s) {
     return G.D >= 1 ? fam_cslot(G, G.firstD) : -1;
 }
 
-// Step 3 after family_select, by the whole block (1 <= n <= cap; pop[0, cap +
-// kPoolPad + kWave) zero on entry): pop index = 1 + the number of pool keys
-// that pop first.  Writes the pop-order records 1..cnt (cnt = min(n, nmax))
-// into par/dep/tok/rho (nmax + 2 entries; index nmax + 1 takes the stores of
-// nodes past cnt) and returns cnt.
+// Step 3 after family_select, by the whole block (1 <= n <= cap <= 1024;
+// L.hist zero on entry; every key has rho >= t): pop index = 1 + the number
+// of pool keys that pop first.  The keys are binned by rho (L.hist: fine
+// bins over [t, 1], as many mantissa bits as 1024 bins hold), every key of a
+// higher bin pops first, and a key is compared only with the keys of its own
+// bin, placed together in L.rho / L.par (free on the family path).  Writes
+// the pop-order records 1..cnt (cnt = min(n, nmax)) into par/dep/tok/rho
+// (nmax + 2 entries; index nmax + 1 takes the stores of nodes past cnt) and
+// returns cnt.
 template <int THREADS>
-__device__ int family_rank(const PoolLds &L, const FamGeom &G, int n, int nmax, int cap,
+__device__ int family_rank(const PoolLds &L, const FamGeom &G, int n, int nmax, float t,
                            int32_t *par, int32_t *dep, int32_t *tok, float *rho,
                            uint64_t *st = nullptr) {
     (void)st;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int tid = threadIdx.x;
     n = __builtin_amdgcn_readfirstlane(n);
-    // task = (node e, part of the keys): P parts per node, as many as the
-    // block holds; part ranges are multiples of 8 keys
-    const int P = n < THREADS ? THREADS / n : 1;
-    const int chunk = ((n + P - 1) / P + 7) & ~7;
-    const float inv_n = 1.0f / float(n);
-    for (int t0 = 0; t0 < n * P; t0 += THREADS) {
-        const int task = t0 + tid;
-        int part = int((float(task) + 0.5f) * inv_n);
-        part = part * n > task ? part - 1 : ((part + 1) * n <= task ? part + 1 : part);
-        const int e = task - part * n;
-        const bool ve = task < n * P;
-        const int f0 = ve ? part * chunk : 0;
-        const int f1 = !ve ? 0 : (f0 + chunk < n ? f0 + chunk : n);
-        // keys past n are zero (below every real key), so the eight loads of
-        // a step need no range test
-        const uint64_t x = ve ? L.key[e] : ~uint64_t(0);   // e < n when ve
-        const uint64_t xm = x | 1023u;
-        int gt = 0, tn = 0, tpa = 1 << 30, tpb = 0;
-        for (int f = f0; f < f1; f += 8) {
-            uint64_t y[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) y[i] = L.key[f + i];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                gt += (y[i] | 1023u) > xm ? 1 : 0;
-                // same rho, depth and token, another node: keys differ in
-                // the identity field only
-                const bool same = ((y[i] ^ x) - 1u) < 1023u;
-                tn += same ? 1 : 0;
-                tpa = min(tpa, same ? f + i : 1 << 30);
-                tpb = same ? f + i : tpb;
-            }
-        }
-        // equal keys (rare): the first and last are known, more are found by
-        // a scan
-        int fs = tpa + 1;
-        for (int it = 0; it < tn; ++it) {
-            int tp = it == 0 ? tpa : tpb;
-            if (it > 0 && it < tn - 1) {
-                while (fs < f1 && !(((L.key[fs] ^ x) - 1u) < 1023u)) ++fs;
-                tp = fs++;
-            }
-            if (fam_tie_before(G, L.key, x, e, L.key[tp], tp)) ++gt;
-        }
-        atomicAdd(L.pop + (ve ? e : cap + kPoolPad + lane), gt);
-    }
-    __syncthreads();
+    bucket_rank<THREADS>(L.key, n, t, L.hist, reinterpret_cast<uint64_t *>(L.rho), L.par, L.pop,
+                         [&](uint64_t x, int e, uint64_t y, int f) {
+                             return fam_tie_before(G, L.key, x, e, y, f);
+                         });
     BASTION_STAMP(st, 13);
     const int cnt = n < nmax ? n : nmax;
     for (int e = tid; e < n; e += THREADS) {

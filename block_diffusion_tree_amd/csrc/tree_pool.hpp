@@ -303,45 +303,115 @@ __device__ int pool_wide(const PoolLds &L, const float *qtab, const int32_t *tta
     return n;
 }
 
-// Step 3, by the whole block (n >= 1): the pop index of every pool node
-// (L.pop) and the pop-order records 1..cnt (cnt = min(n, nmax)) in
-// par/dep/tok/rho.  Nodes are taken 64 per wave; with fewer such groups than
-// waves, the waves of a group split the comparisons and add their counts.
-// Returns cnt.
-template <int THREADS>
-__device__ __forceinline__ int pool_rank(const PoolLds &L, int n, int nmax, int32_t *par,
-                                         int32_t *dep, int32_t *tok, float *rho) {
-    constexpr int W = THREADS / kWave;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-    int np2 = kWave;
-    while (np2 < n) np2 <<= 1;
-    if (L.sbuf && n > kSortMin && np2 <= THREADS) {
-        block_sort_desc<THREADS>(L.sbuf, L.key, n);
-        for (int e = tid; e < n; e += THREADS) L.pop[e] = 1 + sorted_above(L.sbuf, n, L.key[e]);
-    } else {
-        const int groups = (n + kWave - 1) / kWave;
-        const int split = groups >= W ? 1 : W / groups;   // waves per group
-        const int chunk = (n + split - 1) / split;
-        for (int e = tid; e < n; e += THREADS) L.pop[e] = 1;
-        __syncthreads();
-        for (int g0 = wv / split; g0 < groups; g0 += W / split) {
-            const int e = g0 * kWave + lane;
-            const int part = wv % split;
-            const int f0 = part * chunk, f1 = f0 + chunk < n ? f0 + chunk : n;
-            if (e < n) {
-                const int r = count_greater(L.key, f0, f1, L.key[e]);
-                if (r) atomicAdd(L.pop + e, r);
-            }
+// Pop counts of n keys by rho bins, whole block (1 <= n <= 1024; every
+// key's rho >= t): pop[e] = the number of keys that pop before key e.  The
+// bins (bc: kHistBins counters, zero on entry, left non-zero) split [t, 1]
+// as finely as 1024 bins allow (rho bits >> (20 - ex), less t's bin); every
+// key of a higher bin pops first, and a key is compared only with the keys
+// of its own bin, which are first placed together in sb (n entries), their
+// indices in sx (n entries; null when the tie rule needs none).  Keys equal
+// but for their low 10 bits pop in the order before(x, e, y, f) gives (does
+// key y, index f, pop before key x, index e?).
+template <int THREADS, typename Tie>
+__device__ __forceinline__ void bucket_rank(const uint64_t *key, int n, float t, uint32_t *bc,
+                                            uint64_t *sb, int32_t *sx, int32_t *pop, Tie before) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    constexpr int kPer = 1024 / THREADS > 0 ? 1024 / THREADS : 1;
+    const int tbin = int(__float_as_uint(t) >> 20);
+    const int R = 1017 - tbin;   // bins up to rho = 1 (bin 1016)
+    int ex = 0;
+    while (ex < 20 && (R << (ex + 1)) <= kHistBins) ++ex;
+    int arr[kPer], fb[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int e = tid + i * THREADS;
+        fb[i] = 0;
+        arr[i] = 0;
+        if (e < n) {
+            const uint32_t rb = uint32_t(key[e] >> 34) - 1u;   // rho's bits
+            fb[i] = min(max(int(rb >> (20 - ex)) - (tbin << ex), 0), kHistBins - 1);
+            arr[i] = int(atomicAdd(bc + fb[i], 1u));
         }
     }
     __syncthreads();
+    if (tid < kWave) {
+        // bins 16 lane .. 16 lane + 15: counts -> keys in higher bins
+        pool_u32x4 *b4 = reinterpret_cast<pool_u32x4 *>(bc + 16 * lane);
+        uint32_t c[16], own = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const pool_u32x4 v = b4[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c[4 * i + j] = v[j];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) own += c[i];
+        const uint32_t incl = wave_incl_scan_u32(own);
+        uint32_t run = uint32_t(__builtin_amdgcn_readlane(int(incl), kWave - 1)) - incl;
+#pragma unroll
+        for (int i = 15; i >= 0; --i) {
+            const uint32_t ci = c[i];
+            c[i] = run;
+            run += ci;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pool_u32x4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = c[4 * i + j];
+            b4[i] = v;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int e = tid + i * THREADS;
+        if (e < n) {
+            const int slot = int(bc[fb[i]]) + arr[i];
+            sb[slot] = key[e];
+            if (sx) sx[slot] = e;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int e = tid + i * THREADS;
+        if (e < n) {
+            const uint64_t x = key[e], xm = x | 1023u;
+            const int f0 = int(bc[fb[i]]);
+            const int f1 = fb[i] > 0 ? int(bc[fb[i] - 1]) : n;
+            int gt = f0;
+            for (int f = f0; f < f1; ++f) {
+                const uint64_t y = sb[f];
+                if ((y | 1023u) > xm) ++gt;
+                else if (((y ^ x) - 1u) < 1023u && before(x, e, y, sx ? sx[f] : 0)) ++gt;
+            }
+            pop[e] = gt;
+        }
+    }
+    __syncthreads();
+}
+
+// Step 3, by the whole block (1 <= n <= 1024; L.hist zero on entry): the pop
+// index of every pool node (L.pop holds the number of nodes before it) and
+// the pop-order records 1..cnt (cnt = min(n, nmax)) in par/dep/tok/rho, the
+// ranks by rho bins (bucket_rank).  Returns cnt.
+template <int THREADS>
+__device__ __forceinline__ int pool_rank(const PoolLds &L, int n, int nmax, float t,
+                                         int32_t *par, int32_t *dep, int32_t *tok, float *rho) {
+    const int tid = threadIdx.x;
+    // the pool's keys are distinct (the parent field holds the parent's
+    // in-level rank), so the larger key pops first; L.rho and L.lrank
+    // (adjacent, free once the levels are ranked) hold the binned keys
+    bucket_rank<THREADS>(L.key, n, t, L.hist, reinterpret_cast<uint64_t *>(L.rho), nullptr, L.pop,
+                         [](uint64_t x, int, uint64_t y, int) { return y > x; });
     const int cnt = n < nmax ? n : nmax;
     for (int e = tid; e < n; e += THREADS) {
-        const int pe = L.pop[e];
+        const int pe = L.pop[e] + 1;
         if (pe <= cnt) {
             const int ps = L.par[e];
             const uint64_t x = L.key[e];
-            par[pe] = ps < 0 ? 0 : L.pop[ps];
+            par[pe] = ps < 0 ? 0 : L.pop[ps] + 1;
             dep[pe] = tree_key_depth(x);
             tok[pe] = tree_key_token(x);
             rho[pe] = tree_key_rho(x);
