@@ -456,7 +456,7 @@ __host__ __device__ inline int tree_regs(int nmax) {
 
 struct TreeLayout {
     int qtab, ttab, col, par, dep, tok, rho, ahat, cost, map, base;
-    int pkey, ppar, prho, plrank, ppop, psort, hist, plvl, q0col, fwork, total;
+    int pkey, ppar, prho, plrank, ppop, hist, plvl, q0col, fwork, total;
 };
 
 // wide: the pool capacity of the trees' own launch (pool_cap_wide)
@@ -484,7 +484,6 @@ __host__ __device__ inline TreeLayout tree_layout(int b, int k, int nmax, int th
     L.prho = o; o = align16(o + 4 * pslots);
     L.plrank = o; o = align16(o + 4 * pslots);
     L.ppop = o; o = align16(o + 4 * pslots);
-    L.psort = o; o = align16(o + (wide ? 8 * cap : 0));   // sort scratch of large pools
     L.hist = o; o = align16(o + (cap > 0 ? 4 * (kHistBins + kWave) : 0));
     L.plvl = o; o = align16(o + (cap > 0 ? 4 * kLvlFloats : 0));
     L.q0col = o; o = align16(o + 3 * 4 * kColLen);   // FamilyCols q0, q1n, t0
@@ -765,7 +764,6 @@ __device__ __forceinline__ void tree_stage(const BuildParams &P, int q, char *sm
         PL.lrank = reinterpret_cast<int32_t *>(smem + TL.plrank);
         PL.pop = reinterpret_cast<int32_t *>(smem + TL.ppop);
         PL.hist = reinterpret_cast<uint32_t *>(smem + TL.hist);
-        PL.sbuf = WIDE ? reinterpret_cast<uint64_t *>(smem + TL.psort) : nullptr;
         lvl = reinterpret_cast<float *>(smem + TL.plvl);
         F.q0 = fq0;
         F.q1n = fq1n;

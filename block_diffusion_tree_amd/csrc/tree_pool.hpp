@@ -16,17 +16,14 @@
 //      are monotone), so each parent contributes a prefix of its ranks.
 //      Such pools are a few parallel chains that branch at uncertain
 //      positions: one wave follows them, a chain per lane in registers,
-//      while none branches (each child keeps its parent's in-level rank:
-//      same token, monotone rho, and the chains that stop are the last
-//      ones); from the first level where one branches the whole block
-//      expands the levels from LDS and ranks each one.  A node's key holds
-//      its parent's rank inside the parent's level, which is best-first's
-//      order for children of different parents that agree on (rho, depth,
-//      token); keys are then unique and compare exactly as best-first pops.
-//      The caller falls back to the exact round-by-round build if the pool
-//      outgrows its capacity.
-//   3. the block counts, for every pool node, the larger keys; the count is
-//      its pop index minus one, and the first min(pool, N) are the tree.
+//      while none branches; from the first level where one branches the
+//      whole block expands the levels from LDS.  The caller falls back to
+//      the exact round-by-round build if the pool outgrows its capacity.
+//   3. every pool node's pop index is one plus the number of keys that pop
+//      before it, counted by rho bins (bucket_rank); nodes that agree on
+//      (rho, depth, token) pop in their parents' order, found by walking up
+//      both parent chains to the first ancestors that differ.  The first
+//      min(pool, N) are the tree.
 #pragma once
 
 #include "device_common.hpp"
@@ -52,13 +49,14 @@ typedef float pool_f32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t pool_i32x4 __attribute__((ext_vector_type(4)));
 
 struct PoolLds {
-    uint64_t *key;     // [cap] tree_key, parent field = parent's in-level rank
-    int32_t *par;      // [cap] parent slot, -1 for the root
-    float *rho;        // [cap]
-    int32_t *lrank;    // [cap] rank inside its level
+    uint64_t *key;     // [cap] tree_key (the pool's parent field is 0; the
+                       // family's holds the node's family identity)
+    int32_t *par;      // [cap] parent slot, -1 for the root (pool path)
+    float *rho;        // [cap] (pool path)
+    int32_t *lrank;    // [cap] adjacent to rho: with it, bucket_rank's
+                       // placement of up to cap 64-bit keys
     int32_t *pop;      // [cap] pop index
     uint32_t *hist;    // [kHistBins]
-    uint64_t *sbuf;    // [cap] sort scratch (trees' own launch), or null
 };
 
 
@@ -76,86 +74,9 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
     return v + (row > 0 ? r0 : 0u) + (row > 1 ? r1 : 0u) + (row > 2 ? r2 : 0u);
 }
 
-// number of keys[f0..f1) greater than x; eight loads in flight at a time
-__device__ __forceinline__ int count_greater(const uint64_t *keys, int f0, int f1, uint64_t x) {
-    int r = 0;
-    for (int f = f0; f < f1; f += 8) {
-        uint64_t y[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = keys[f + i < f1 ? f + i : f1 - 1];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) r += (f + i < f1 && y[i] > x) ? 1 : 0;
-    }
-    return r;
-}
-
-// Large pools and levels are ranked by sorting instead of counting every
-// pair: a bitonic sort of the keys over the whole block (partners inside a
-// wave through DPP / permlane swaps, across waves through LDS), then each
-// key's place by binary search in the sorted copy.  Used past kSortMin keys
-// when the block holds the next power of two.
-constexpr int kSortMin = 512;
-
-// sbuf[0, M) = keys[0, m) in descending order, zeros after (M: the power of
-// two >= max(m, 64), at most THREADS; sbuf apart from keys).  Whole block;
-// ends with a barrier.
-template <int THREADS>
-__device__ void block_sort_desc(uint64_t *sbuf, const uint64_t *keys, int m) {
-    const int tid = threadIdx.x;
-    int M = kWave;
-    while (M < m) M <<= 1;
-    const bool act = tid < M;
-    const uint64_t x0 = tid < m ? keys[tid] : uint64_t(0);
-    uint32_t h = uint32_t(x0 >> 32), l = uint32_t(x0);
-    for (int k = 2; k <= M; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const bool desc = (tid & k) == 0;
-            if (j >= kWave) {
-                if (act) sbuf[tid] = (uint64_t(h) << 32) | l;
-                __syncthreads();
-                if (act) {
-                    const uint64_t o = sbuf[tid ^ j];
-                    const uint32_t oh = uint32_t(o >> 32), ol = uint32_t(o);
-                    const bool ogt = key_gt(oh, ol, h, l);
-                    const bool lower = (tid & j) == 0;
-                    const bool take = (desc == lower) ? ogt : !ogt;
-                    h = take ? oh : h;
-                    l = take ? ol : l;
-                }
-                __syncthreads();
-            } else if (j == 32) {
-                cmpx<32>(h, l, desc);
-            } else if (j == 16) {
-                cmpx<16>(h, l, desc);
-            } else if (j == 8) {
-                cmpx<8>(h, l, desc);
-            } else if (j == 4) {
-                cmpx<4>(h, l, desc);
-            } else if (j == 2) {
-                cmpx<2>(h, l, desc);
-            } else {
-                cmpx<1>(h, l, desc);
-            }
-        }
-    }
-    if (act) sbuf[tid] = (uint64_t(h) << 32) | l;
-    __syncthreads();
-}
-
-// number of keys above x in sbuf[0, m), sorted descending
-__device__ __forceinline__ int sorted_above(const uint64_t *sbuf, int m, uint64_t x) {
-    int lo = 0, hi = m;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (sbuf[mid] > x) lo = mid + 1;
-        else hi = mid;
-    }
-    return lo;
-}
-
 // Where the one-wave enumeration stops: the first level where a chain
-// branches (its parents [lo, hi), ranked inside their level, d its depth);
-// the block continues there (pool_wide).
+// branches (its parents [lo, hi), d its depth); the block continues there
+// (pool_wide).
 struct PoolWide {
     int lo, hi, d;
     bool wide;
@@ -185,11 +106,10 @@ __device__ int pool_enumerate(const PoolLds &L, const float *qtab, const int32_t
         L.key[lane] = tree_key(q1v, 1, ttab[lane], 0);
         L.par[lane] = -1;
         L.rho[lane] = q1v;
-        L.lrank[lane] = lane;
     }
     bool alive = ok1;
     float rho = q1v;
-    int slot = lane, lr = lane;
+    int slot = lane;
     int lo = 0, hi = n, d = 2;
     bool wide = false, over = false;
     // chains in lanes
@@ -200,8 +120,7 @@ __device__ int pool_enumerate(const PoolLds &L, const float *qtab, const int32_t
         const bool ok0 = alive && v0 >= t;
         const bool br = alive && k > 1 && __fmul_rn(rho, q1) >= t;
         if (__ballot(br) == 0) {
-            // no chain branches: each continues with its rank-0 child, which
-            // keeps the parent's in-level rank
+            // no chain branches: each continues with its rank-0 child
             const uint64_t m = __ballot(ok0);
             const int c = __builtin_amdgcn_readfirstlane(popc64(m));
             if (n + c > cap) {
@@ -211,10 +130,9 @@ __device__ int pool_enumerate(const PoolLds &L, const float *qtab, const int32_t
             const int s = n + popc64(m & lt);
             const int t0 = __builtin_amdgcn_readlane(tok0, d - 1);
             if (ok0) {
-                L.key[s] = tree_key(v0, d, t0, lr);
+                L.key[s] = tree_key(v0, d, t0, 0);
                 L.par[s] = slot;
                 L.rho[s] = v0;
-                L.lrank[s] = lr;
             }
             alive = ok0;
             rho = v0;
@@ -238,10 +156,9 @@ __device__ int pool_enumerate(const PoolLds &L, const float *qtab, const int32_t
 // Step 2 continued, by the whole block, from the first branching level: each
 // thread takes rank j (of k rounded up to a power of two) of one parent;
 // the level's qualifying children get slots through a block-wide prefix of
-// the waves' ballots, then every thread ranks some of them inside the level
-// (slot order within a level is free: the in-level rank orders the keys).
-// Returns the node count, or -1 past cap (block-uniform).  Ends with a
-// barrier.
+// the waves' ballots (slot order within a level is free: step 3 orders the
+// keys).  Returns the node count, or -1 past cap (block-uniform).  Ends
+// with a barrier.
 template <int THREADS>
 __device__ int pool_wide(const PoolLds &L, const float *qtab, const int32_t *ttab, int b, int k,
                          int kp, float t, int cap, int lo, int hi, int d, int n) {
@@ -264,7 +181,6 @@ __device__ int pool_wide(const PoolLds &L, const float *qtab, const int32_t *tta
             const bool valid = p < np && j < k;
             const int pc = lo + (p < np ? p : np - 1);
             const float v = __fmul_rn(L.rho[pc], qj);
-            const int pr = L.lrank[pc];
             const bool ok = valid && v >= t;
             const uint64_t m = __ballot(ok);
             if (lane == 0) s_cnt[wv] = popc64(m);
@@ -279,24 +195,13 @@ __device__ int pool_wide(const PoolLds &L, const float *qtab, const int32_t *tta
             if (n + tot > cap) return -1;
             if (ok) {
                 const int s = n + before + popc64(m & lt);
-                L.key[s] = tree_key(v, d, tj, pr);
+                L.key[s] = tree_key(v, d, tj, 0);
                 L.par[s] = pc;
                 L.rho[s] = v;
             }
             n += tot;
             __syncthreads();   // the counts are read; the level's keys are written
         }
-        const int m = n - n0;
-        int mp = kWave;
-        while (mp < m) mp <<= 1;
-        if (L.sbuf && m > kSortMin && mp <= THREADS) {
-            block_sort_desc<THREADS>(L.sbuf, L.key + n0, m);
-            for (int s = n0 + tid; s < n; s += THREADS) L.lrank[s] = sorted_above(L.sbuf, m, L.key[s]);
-        } else {
-            for (int s = n0 + tid; s < n; s += THREADS)
-                L.lrank[s] = count_greater(L.key, n0, n, L.key[s]);
-        }
-        __syncthreads();
         lo = n0;
         hi = n;
     }
@@ -304,18 +209,42 @@ __device__ int pool_wide(const PoolLds &L, const float *qtab, const int32_t *tta
 }
 
 // Pop counts of n keys by rho bins, whole block (1 <= n <= 1024; every
-// key's rho >= t): pop[e] = the number of keys that pop before key e.  The
+// key's rho >= t; pop zero on entry): pop[e] = the number of keys that pop
+// before key e.  The
 // bins (bc: kHistBins counters, zero on entry, left non-zero) split [t, 1]
 // as finely as 1024 bins allow (rho bits >> (20 - ex), less t's bin); every
 // key of a higher bin pops first, and a key is compared only with the keys
-// of its own bin, which are first placed together in sb (n entries), their
-// indices in sx (n entries; null when the tie rule needs none).  Keys equal
-// but for their low 10 bits pop in the order before(x, e, y, f) gives (does
-// key y, index f, pop before key x, index e?).
+// of its own bin, which are first placed together in sb (n entries) with
+// their indices: in sx, or, when sx is null, in the keys' low 10 bits (which
+// the comparisons then ignore).  Keys equal but for their low 10 bits pop
+// in the order before(x, e, y, f) gives (does key y, index f, pop before
+// key x, index e?).
+// Up to kPairMax keys are instead compared all with all, each key's count
+// split over THREADS / n threads (pop zero on entry; bc untouched).
+constexpr int kPairMax = 64;
+
 template <int THREADS, typename Tie>
 __device__ __forceinline__ void bucket_rank(const uint64_t *key, int n, float t, uint32_t *bc,
                                             uint64_t *sb, int32_t *sx, int32_t *pop, Tie before) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    if (n <= kPairMax) {
+        const int P = THREADS / n;   // parts per key
+        const int chunk = (n + P - 1) / P;
+        const int e = tid % n, part = tid / n;
+        if (part < P) {
+            const uint64_t x = key[e], xm = x | 1023u;
+            const int f0 = part * chunk, f1 = f0 + chunk < n ? f0 + chunk : n;
+            int gt = 0;
+            for (int f = f0; f < f1; ++f) {
+                const uint64_t y = key[f], ym = y | 1023u;
+                if (ym > xm) ++gt;
+                else if (ym == xm && f != e && before(x, e, y, f)) ++gt;
+            }
+            if (gt) atomicAdd(pop + e, gt);
+        }
+        __syncthreads();
+        return;
+    }
     constexpr int kPer = 1024 / THREADS > 0 ? 1024 / THREADS : 1;
     const int tbin = int(__float_as_uint(t) >> 20);
     const int R = 1017 - tbin;   // bins up to rho = 1 (bin 1016)
@@ -368,8 +297,12 @@ __device__ __forceinline__ void bucket_rank(const uint64_t *key, int n, float t,
         const int e = tid + i * THREADS;
         if (e < n) {
             const int slot = int(bc[fb[i]]) + arr[i];
-            sb[slot] = key[e];
-            if (sx) sx[slot] = e;
+            if (sx) {
+                sb[slot] = key[e];
+                sx[slot] = e;
+            } else {
+                sb[slot] = (key[e] & ~uint64_t(1023)) | uint64_t(e);
+            }
         }
     }
     __syncthreads();
@@ -382,9 +315,14 @@ __device__ __forceinline__ void bucket_rank(const uint64_t *key, int n, float t,
             const int f1 = fb[i] > 0 ? int(bc[fb[i] - 1]) : n;
             int gt = f0;
             for (int f = f0; f < f1; ++f) {
-                const uint64_t y = sb[f];
-                if ((y | 1023u) > xm) ++gt;
-                else if (((y ^ x) - 1u) < 1023u && before(x, e, y, sx ? sx[f] : 0)) ++gt;
+                const uint64_t y = sb[f], ym = y | 1023u;
+                if (ym > xm) {
+                    ++gt;
+                } else if (ym == xm) {
+                    // same rho, depth and token: another node?
+                    const int fi = sx ? sx[f] : int(y & 1023u);
+                    if (fi != e && before(x, e, y, fi)) ++gt;
+                }
             }
             pop[e] = gt;
         }
@@ -400,11 +338,20 @@ template <int THREADS>
 __device__ __forceinline__ int pool_rank(const PoolLds &L, int n, int nmax, float t,
                                          int32_t *par, int32_t *dep, int32_t *tok, float *rho) {
     const int tid = threadIdx.x;
-    // the pool's keys are distinct (the parent field holds the parent's
-    // in-level rank), so the larger key pops first; L.rho and L.lrank
-    // (adjacent, free once the levels are ranked) hold the binned keys
+    // equal (rho, depth, token): the parents' order, from the first
+    // ancestors (same depth) whose keys differ; L.rho and L.lrank (adjacent,
+    // free once the pool is enumerated) hold the binned keys
     bucket_rank<THREADS>(L.key, n, t, L.hist, reinterpret_cast<uint64_t *>(L.rho), nullptr, L.pop,
-                         [](uint64_t x, int, uint64_t y, int) { return y > x; });
+                         [&](uint64_t, int e, uint64_t, int f) {
+                             int a = L.par[e], c = L.par[f];
+                             while (a != c && a >= 0 && c >= 0) {
+                                 const uint64_t ka = L.key[a] | 1023u, kc = L.key[c] | 1023u;
+                                 if (ka != kc) return kc > ka;
+                                 a = L.par[a];
+                                 c = L.par[c];
+                             }
+                             return false;
+                         });
     const int cnt = n < nmax ? n : nmax;
     for (int e = tid; e < n; e += THREADS) {
         const int pe = L.pop[e] + 1;
