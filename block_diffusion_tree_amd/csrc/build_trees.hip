@@ -840,6 +840,8 @@ __device__ __forceinline__ void tree_stage(const BuildParams &P, int q, char *sm
                         s_pw[1] = pw.hi;
                         s_pw[2] = pw.wide ? pw.d : 0;
                     }
+                    if (NT == kWave)
+                        for (int i = lane; i < kHistBins; i += kWave) PL.hist[i] = 0u;
                 } else {
                     // meanwhile the other waves clear pool_rank's bins
                     for (int i = tid - kWave; i < kHistBins; i += NT - kWave) PL.hist[i] = 0u;
