@@ -328,6 +328,32 @@ def test_row_stride_padding_and_pos_base():
     gc.check_mask(g, pos_base)
 
 
+def test_calls_on_two_streams_match_the_serial_calls():
+    """Two batches in flight: calls alternate between two streams, each with
+    its own workspace and outputs (the benchmark's two-in-flight rate runs
+    this); every output equals the one-call-at-a-time result."""
+    wl = synth.scaled(synth.WORKLOADS["main"], B=16, V=32768)
+    xs = [synth.make_logits(wl, device="cuda", seed=wl.seed + i) for i in range(4)]
+    serial = [binding.build_trees(x, k=wl.k, nmax=wl.nmax) for x in xs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [binding.Workspace(torch.device("cuda:0")) for _ in streams]
+    outs, calls = [], []
+    for i in range(8):
+        with torch.cuda.stream(streams[i % 2]):
+            o, c = binding.prepare_build_trees(xs[i % 4], k=wl.k, nmax=wl.nmax, ws=wss[i % 2])
+        outs.append(o)
+        calls.append(c)
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        ref = serial[i % 4]
+        for f in ("topk_ids", "topk_q", "row_max", "row_sum", "parent", "depth", "token", "rho",
+                  "ahat", "n_nodes", "qstatus", "mask", "position_ids"):
+            assert torch.equal(o[f], ref[f]), (i, f)
+
+
 def test_workspace_reuse_across_shapes():
     ws = binding.Workspace()
     a = synth.scaled(synth.WORKLOADS["main"], B=4, b=16, V=40000, nmax=30)
