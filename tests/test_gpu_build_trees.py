@@ -228,6 +228,7 @@ def test_one_hot_rows_give_a_chain_then_zero_mass():
 @pytest.mark.parametrize("shape", [
     dict(b=1, k=6, V=6, nmax=4),             # star, V == k, all in the scalar tail
     dict(b=5, k=1, V=5, nmax=10),            # greedy chain, exhausted
+    dict(b=3, k=5, V=300, nmax=200),         # whole tree (155 nodes) below the budget
     dict(b=32, k=2, V=777, nmax=1023),       # deepest block, largest budget
     dict(b=3, k=32, V=4099, nmax=200),       # widest candidate lists
     dict(b=32, k=32, V=4099, nmax=512),      # deepest and widest: tree LDS above 64 KiB
