@@ -332,14 +332,31 @@ __device__ __forceinline__ SegmentResult stream_segment(const BuildParams &P, co
         fill(A, okA, 0);
         // The instruction arbiter favours older waves, so the blocks sharing
         // a CU would otherwise finish one after another and leave the CU
-        // with a single streaming block at the end.  A wave's priority falls
-        // as its segment progresses (four tiers), which keeps the
-        // co-resident blocks level.  (A later start for blocks dispatched
-        // later, one tier per quarter of the grid, measured 1.2 us slower at
-        // the 64 x 16 x 151936 bf16 workload.)
+        // with a single streaming block at the end.  When the grid fits the
+        // machine at once and the segments are long (8 tiles or more: the
+        // short ones are latency-bound), each block keeps to a schedule: its
+        // share of 6.4 TB/s among the blocks, timed from its start on the
+        // 100 MHz real-time counter; a block behind it raises its priority,
+        // one ahead of it lowers it (four tiers), which keeps the
+        // co-resident blocks level.  Otherwise (larger grids run in rounds
+        // of blocks that start at different times) a wave's priority falls
+        // as its segment progresses.  (Progress tiers: 0.8 us slower on the
+        // 64 x 16 x 151936 bf16 workload; the schedule: 5 us slower on the
+        // 256 x 16 x 128256 fp32 sweep, 10 us on the 8-branch mixture; a
+        // later start for blocks dispatched later: 1.2 us slower.)
         int tier = -1;
+        const bool sched = int(gridDim.x) <= P.resident_blocks && ntot >= 8;
+        const uint64_t clk0 = __builtin_amdgcn_s_memrealtime();
+        const int64_t tick_pair = int64_t(2) * span * 16 * int(gridDim.x) / 64000;   // 10 ns ticks
         for (int t = 0; t < ntot; t += 2) {
-            const int nt = (4 * t) / ntot;
+            int nt;
+            if (sched) {
+                const int64_t lag =
+                    int64_t(__builtin_amdgcn_s_memrealtime() - clk0) - int64_t(t / 2) * tick_pair;
+                nt = lag > tick_pair ? 0 : lag > 0 ? 1 : lag > -tick_pair ? 2 : 3;
+            } else {
+                nt = (4 * t) / ntot;
+            }
             if (nt != tier) {
                 tier = nt;
                 if (nt == 0) __builtin_amdgcn_s_setprio(3);
