@@ -235,10 +235,18 @@ __device__ __forceinline__ void bucket_rank(const uint64_t *key, int n, float t,
             const uint64_t x = key[e], xm = x | 1023u;
             const int f0 = part * chunk, f1 = f0 + chunk < n ? f0 + chunk : n;
             int gt = 0;
+            uint64_t ties = 0;   // chunk <= n <= 64
             for (int f = f0; f < f1; ++f) {
-                const uint64_t y = key[f], ym = y | 1023u;
-                if (ym > xm) ++gt;
-                else if (ym == xm && f != e && before(x, e, y, f)) ++gt;
+                const uint64_t ym = key[f] | 1023u;
+                gt += ym > xm ? 1 : 0;
+                ties |= uint64_t(ym == xm && f != e) << (f - f0);
+            }
+            // equal keys after the scan, one partner per lane at a time: the
+            // wave walks parents as often as its lane with the most ties
+            while (ties) {
+                const int f = f0 + __builtin_ctzll(ties);
+                ties &= ties - 1;
+                if (before(x, e, key[f], f)) ++gt;
             }
             if (gt) atomicAdd(pop + e, gt);
         }
@@ -313,15 +321,24 @@ __device__ __forceinline__ void bucket_rank(const uint64_t *key, int n, float t,
             const uint64_t x = key[e], xm = x | 1023u;
             const int f0 = int(bc[fb[i]]);
             const int f1 = fb[i] > 0 ? int(bc[fb[i] - 1]) : n;
+            const int self = f0 + arr[i];   // where the placement put key e
             int gt = f0;
-            for (int f = f0; f < f1; ++f) {
-                const uint64_t y = sb[f], ym = y | 1023u;
-                if (ym > xm) {
-                    ++gt;
-                } else if (ym == xm) {
-                    // same rho, depth and token: another node?
-                    const int fi = sx ? sx[f] : int(y & 1023u);
-                    if (fi != e && before(x, e, y, fi)) ++gt;
+            // 64 places of the bin at a time: count the larger keys, mark the
+            // equal ones (same rho, depth and token), then order those by
+            // their parents, one partner per lane at a time
+            for (int w0 = f0; w0 < f1; w0 += kWave) {
+                const int w1 = w0 + kWave < f1 ? w0 + kWave : f1;
+                uint64_t ties = 0;
+                for (int f = w0; f < w1; ++f) {
+                    const uint64_t ym = sb[f] | 1023u;
+                    gt += ym > xm ? 1 : 0;
+                    ties |= uint64_t(ym == xm && f != self) << (f - w0);
+                }
+                while (ties) {
+                    const int f = w0 + __builtin_ctzll(ties);
+                    ties &= ties - 1;
+                    const uint64_t y = sb[f];
+                    if (before(x, e, y, sx ? sx[f] : int(y & 1023u))) ++gt;
                 }
             }
             pop[e] = gt;
