@@ -450,9 +450,30 @@ __device__ int family_select(const PoolLds &L, const float *qtab, const int32_t 
         }
     }
     // the paths, by their owners: nodes dstart .. dstart + cn - 1
+    // (blocks of up to 256 threads: the wider blocks of the trees' own
+    // launch have no registers to spare for it and walk the path again)
+    constexpr bool kRegWrites = THREADS <= 256;
+    if (kRegWrites && rounds == 1 && b <= 16) {
+        // the path's rho at every depth is still in registers from
+        // family_bound's walk: every node's key at once, tokens by 16-byte
+        // column loads
+        const Chain c = make_chain(tid, npair, b, k, kp, D, inv_km1, qtab, ttab);
+        const int s0 = baseB + __builtin_amdgcn_readlane(wpre, wv) + cbase[0];
+        const int code = c.top ? 0 : (c.e - 1) * 32 + c.j;
+        const int cnc = cn[0] < cap - s0 ? cn[0] : cap - s0;
+        pool_i32x4 t4[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) t4[g] = *reinterpret_cast<const pool_i32x4 *>(F.t0 + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int d = i + 1, off = d - c.dstart;
+            const int tk = d == c.e ? c.te : t4[i >> 2][i & 3];
+            L.key[off >= 0 && off < cnc ? s0 + off : dummy] = fam_key(R.rv[i], d, tk, code);
+        }
+    }
 #pragma unroll
     for (int rd = 0; rd < kFamRounds; ++rd) {
-        if (rd < rounds) {
+        if (rd < rounds && !(kRegWrites && rounds == 1 && b <= 16)) {
             const Chain c = make_chain(rd * THREADS + tid, npair, b, k, kp, D, inv_km1, qtab, ttab);
             const int s0 = baseB + __builtin_amdgcn_readlane(wpre, rd * W + wv) + cbase[rd];
             const int code = c.top ? 0 : (c.e - 1) * 32 + c.j;
